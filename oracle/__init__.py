@@ -1,0 +1,176 @@
+"""Double-precision CPU oracle for the LTX-2 per-block attention set.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does.  It
+shares no code with the HIP library and imports nothing from it.
+
+The arithmetic lives in ``ltxattn_oracle.c`` (softmax(Q K^T / sqrt(D)) V in
+IEEE double, one row at a time).  This module only marshals arrays and
+applies the stream pairing of the four attentions that every block of the
+joint video+audio DiT runs (TensorRT-LLM PR #16228 "LTX-2: replicate audio
+stream across Ulysses ranks by default", section "Description"):
+
+============  =========  ==========  =====================
+kind          queries    keys/values  valid keys
+============  =========  ==========  =====================
+video_self    video      video       all video tokens
+audio_self    audio      audio       ``audio_kv_len``
+a2v           video      audio       ``audio_kv_len``
+v2a           audio      video       all video tokens
+============  =========  ==========  =====================
+
+Audio keys at or beyond ``audio_kv_len`` are padding (the audio stream is
+padded, same PR, "Description") and get weight exactly zero.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ltxattn_oracle.c")
+_LIB = os.path.join(_HERE, "libltxattn_oracle.so")
+_lib = None
+
+KINDS = ("video_self", "audio_self", "a2v", "v2a")
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (-O2, no fast-math).  Returns the .so path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                        "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.ltxattn_oracle_attention.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64,
+                                                 p, p, ctypes.c_int]
+        lib.ltxattn_oracle_attention.restype = ctypes.c_int
+        lib.ltxattn_oracle_attention_rows.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64,
+                                                      p, i64, p, p, ctypes.c_int]
+        lib.ltxattn_oracle_attention_rows.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _as_f32(x: np.ndarray) -> np.ndarray:
+    """bf16 bits (uint16) are widened to float32 exactly; float arrays must
+    already hold the values to use."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    if x.dtype == np.float32:
+        return np.ascontiguousarray(x)
+    if x.dtype == np.float64:
+        f = x.astype(np.float32)
+        if not np.array_equal(f.astype(np.float64), x):
+            raise ValueError("float64 input is not exactly representable in float32")
+        return f
+    raise TypeError(f"unsupported dtype {x.dtype}")
+
+
+def _shapes(q, k, v, kv_len):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, S, H, D]")
+    B, Sq, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != (H, D):
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    Sk = k.shape[1]
+    kv_len = Sk if kv_len is None else int(kv_len)
+    if not 1 <= kv_len <= Sk:
+        raise ValueError(f"kv_len {kv_len} outside [1, {Sk}]")
+    return B, Sq, Sk, kv_len, H, D
+
+
+def attention(q, k, v, kv_len=None, threads=None, return_lse=False):
+    """softmax(q k^T / sqrt(D)) v over keys j < kv_len, in double.
+
+    q: [B, Sq, H, D]; k, v: [B, Sk, H, D] (bf16 bits or float32 values).
+    Returns o [B, Sq, H, D] float64 (and lse [B, Sq, H] if asked).
+    """
+    q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
+    B, Sq, Sk, L, H, D = _shapes(q, k, v, kv_len)
+    out = np.empty((B, Sq, H, D), dtype=np.float64)
+    lse = np.empty((B, Sq, H), dtype=np.float64) if return_lse else None
+    rc = _load().ltxattn_oracle_attention(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, Sq, Sk, L, H, D,
+        out.ctypes.data, lse.ctypes.data if lse is not None else None,
+        threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle failed with {rc}")
+    return (out, lse) if return_lse else out
+
+
+def attention_rows(q, k, v, rows, kv_len=None, threads=None, return_lse=False):
+    """Same as :func:`attention` for selected rows only.
+
+    rows: int array [n, 3] of (b, h, i).  Returns o [n, D] float64 (and lse [n]).
+    """
+    q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
+    B, Sq, Sk, L, H, D = _shapes(q, k, v, kv_len)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+    n = rows.shape[0]
+    out = np.empty((n, D), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64) if return_lse else None
+    rc = _load().ltxattn_oracle_attention_rows(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, Sq, Sk, L, H, D,
+        rows.ctypes.data, n, out.ctypes.data,
+        lse.ctypes.data if lse is not None else None, threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle failed with {rc}")
+    return (out, lse) if return_lse else out
+
+
+def pairing(kind: str, inputs: dict, audio_kv_len: int):
+    """(q, k, v, kv_len) of attention ``kind`` from the six stream tensors."""
+    vq, vk, vv = inputs["video_q"], inputs["video_k"], inputs["video_v"]
+    aq, ak, av = inputs["audio_q"], inputs["audio_k"], inputs["audio_v"]
+    if kind == "video_self":
+        return vq, vk, vv, vk.shape[1]
+    if kind == "audio_self":
+        return aq, ak, av, audio_kv_len
+    if kind == "a2v":
+        return vq, ak, av, audio_kv_len
+    if kind == "v2a":
+        return aq, vk, vv, vk.shape[1]
+    raise ValueError(kind)
+
+
+def block_attention(inputs: dict, audio_kv_len: int, kinds=KINDS, threads=None):
+    """All four attentions of one block; returns {kind: o float64 [B, Sq, H, D]}."""
+    out = {}
+    for kind in kinds:
+        q, k, v, L = pairing(kind, inputs, audio_kv_len)
+        out[kind] = attention(q, k, v, kv_len=L, threads=threads)
+    return out
+
+
+def block_attention_rows(inputs: dict, audio_kv_len: int, rows: dict, threads=None):
+    """Selected rows of each attention: rows = {kind: int array [n, 3] of (b, h, i)}."""
+    out = {}
+    for kind, r in rows.items():
+        q, k, v, L = pairing(kind, inputs, audio_kv_len)
+        out[kind] = attention_rows(q, k, v, r, kv_len=L, threads=threads)
+    return out
