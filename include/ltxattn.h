@@ -1,0 +1,166 @@
+/*
+ * ltxattn.h -- C ABI of the per-block attention set of the LTX-2 joint
+ * video+audio DiT, for AMD Instinct MI355X (gfx950).
+ *
+ * Every block of the joint DiT runs four softmax attentions,
+ * O = softmax(Q K^T / sqrt(D)) V, over two token streams (TensorRT-LLM
+ * PR #16228 "LTX-2: replicate audio stream across Ulysses ranks by
+ * default", section "Description", names them and their pairing):
+ *
+ *   LTXATTN_VIDEO_SELF  video queries over video keys/values (the long one:
+ *                       15360 tokens for a 768x1280x121 clip)
+ *   LTXATTN_AUDIO_SELF  audio queries over audio keys/values (126 tokens)
+ *   LTXATTN_A2V         video queries over audio keys/values
+ *   LTXATTN_V2A         audio queries over video keys/values
+ *
+ * The audio stream is padded (same PR, "Description": audio is padded to a
+ * multiple of the sequence-parallel degree), so the caller passes the
+ * number of valid audio keys; audio key rows at or beyond it get weight
+ * exactly zero and are never read.  Padded audio query rows are computed
+ * like any other row.  Q and K arrive already normalised and rotated (the
+ * context-parallel DiT of TensorRT-Model-Connect PR #1586 gathers the
+ * "normed and rotated" keys), so no norm or RoPE happens here.
+ *
+ * Precision: bf16 inputs and outputs with fp32 accumulation and fp32
+ * softmax statistics (the DiT of PR #1586 is bf16 strongly typed with fp32
+ * islands).  Outputs are rounded to bf16 to nearest even.
+ *
+ * Layout: every tensor is [B, S, H, D] bf16 with D contiguous (stride 1)
+ * and explicit batch/sequence/head strides in elements, so both the packed
+ * token-major layout and [B, H, S, D] are accepted.
+ *
+ * Ownership and execution: the caller allocates and owns every tensor and
+ * the stream; the library keeps no pointer past the call.  A call only
+ * enqueues work on the given HIP stream and returns; there is no host
+ * synchronisation inside.  A handle owns its device workspace and is not
+ * thread-safe: use one handle per stream.
+ *
+ * Errors: every entry point returns an int status (LTXATTN_OK = 0).  All
+ * arguments are validated before anything is enqueued, so a rejected call
+ * has no effect on the device.  Nothing is printed, no exception crosses
+ * the ABI and the library never aborts the process.
+ */
+#ifndef LTXATTN_H
+#define LTXATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define LTXATTN_OK               0
+#define LTXATTN_ERR_INVALID_ARG (-1) /* null/misaligned pointer, bad stride, size out of range,
+                                        output overlapping another tensor */
+#define LTXATTN_ERR_UNSUPPORTED (-2) /* head_dim not 64 or 128, heads < 1, tensor too large
+                                        for 32-bit buffer offsets */
+#define LTXATTN_ERR_HIP         (-3) /* a HIP call or kernel launch failed; see
+                                        ltxattn_last_hip_error */
+#define LTXATTN_ERR_OOM         (-4) /* device workspace allocation failed */
+
+/* Attention kinds (index into ltxattn_block_io.attn). */
+enum {
+    LTXATTN_VIDEO_SELF = 0,
+    LTXATTN_AUDIO_SELF = 1,
+    LTXATTN_A2V = 2,
+    LTXATTN_V2A = 3,
+    LTXATTN_NUM_KINDS = 4
+};
+
+typedef struct ltxattn_handle ltxattn_handle;
+
+/* Fixed at create time.  heads and head_dim are shared by all four
+ * attentions.  The max_* capacities bound every later call and size the
+ * device workspace of the split-KV v2a path. */
+typedef struct {
+    int32_t device;        /* HIP device ordinal the handle and its kernels use */
+    int32_t heads;         /* H >= 1 */
+    int32_t head_dim;      /* D, 64 or 128 */
+    int32_t max_batch;     /* >= 1 */
+    int32_t max_video_len; /* >= 1, video tokens */
+    int32_t max_audio_len; /* >= 1, audio buffer rows (padded length) */
+} ltxattn_config;
+
+/* One bf16 tensor [B, S, H, D], D contiguous.  data is a device pointer,
+ * 16-byte aligned; strides are in elements and must be multiples of 8 with
+ * stride_s >= D and stride_h >= D.  Caller-owned. */
+typedef struct {
+    void *data;
+    int64_t stride_b, stride_s, stride_h;
+} ltxattn_tensor;
+
+typedef struct {
+    ltxattn_tensor q, k, v, o;
+} ltxattn_attn_io;
+
+/* One block call.  Row counts by kind:
+ *   VIDEO_SELF: q, k, v, o have video_len rows;
+ *   AUDIO_SELF: q, k, v, o have audio_len rows;
+ *   A2V: q, o have video_len rows, k, v have audio_len rows;
+ *   V2A: q, o have audio_len rows, k, v have video_len rows.
+ * Keys j >= audio_kv_len are masked whenever K/V are audio (AUDIO_SELF, A2V);
+ * 1 <= audio_kv_len <= audio_len.  An entry with o.data == NULL is skipped.
+ * The four entries may share input tensors (the usual case: one video and
+ * one audio Q/K/V triple); an output may not overlap any input or other
+ * output of the call. */
+typedef struct {
+    int32_t batch;
+    int32_t video_len;
+    int32_t audio_len;
+    int32_t audio_kv_len;
+    ltxattn_attn_io attn[LTXATTN_NUM_KINDS];
+} ltxattn_block_io;
+
+/* Create a handle on cfg->device and allocate its workspace.
+ * On success *out receives the handle; on failure *out is set to NULL.
+ * Errors: INVALID_ARG (null pointer, capacity < 1, device out of range),
+ * UNSUPPORTED (head_dim, heads), HIP, OOM. */
+int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out);
+
+/* Enqueue the block's attentions on hip_stream (a hipStream_t; NULL is the
+ * default stream), in the fixed order VIDEO_SELF, A2V, V2A, AUDIO_SELF.
+ * V2A runs as a split-KV pass writing fp32 partial results and softmax
+ * statistics into the handle's workspace, then a combine pass that merges
+ * them by log-sum-exp in a fixed order; the other kinds write bf16 O
+ * directly.  Results are bit-identical from run to run.
+ * Errors: INVALID_ARG, UNSUPPORTED (checked before any launch), HIP. */
+int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void *hip_stream);
+
+/* Validate a block call against a configuration without touching any
+ * device: returns exactly the status ltxattn_block_attention would return
+ * from its argument checks (LTXATTN_OK if the call would be launched).
+ * Lets a caller check a request up front, and the checks be tested on a
+ * machine without a GPU. */
+int ltxattn_check_block(const ltxattn_config *cfg, const ltxattn_block_io *io);
+
+/* Free the workspace and the handle.  The caller must make sure no work
+ * enqueued with the handle is still running.  NULL is accepted. */
+int ltxattn_destroy(ltxattn_handle *h);
+
+/* Static description of a status code. */
+const char *ltxattn_status_string(int status);
+
+/* The hipError_t behind the last LTXATTN_ERR_HIP (or OOM) returned for
+ * this handle; with h == NULL, that of the last failed ltxattn_create on
+ * the calling thread.  0 if none. */
+int ltxattn_last_hip_error(const ltxattn_handle *h);
+
+/* Per-kind timing with HIP events recorded on the call's stream.
+ * ltxattn_profile_begin creates events for up to max_calls block calls
+ * (created here, outside any timed region); each later block call records
+ * one event before the first kind and one after each kind.
+ * ltxattn_profile_read waits for the recorded events and writes, for each
+ * recorded call c < *n_calls (at most max_calls), ms[c*5 + kind] = the time
+ * of that kind (0 if skipped) and ms[c*5 + 4] = the whole call.
+ * ltxattn_profile_end stops recording and frees the events.
+ * Errors: INVALID_ARG (null pointer, max_calls < 1), HIP. */
+int ltxattn_profile_begin(ltxattn_handle *h, int32_t max_calls);
+int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_t *n_calls);
+int ltxattn_profile_end(ltxattn_handle *h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LTXATTN_H */

@@ -1,0 +1,184 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad requests before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+lt = pytest.importorskip("video_audio_diffusion_ltxattn_amd.ltxattn",
+                         reason="libltxattn.so not built")
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(ltxattn_\w+)\s*\(", text))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"ltxattn_create", "ltxattn_block_attention", "ltxattn_destroy"} <= names
+    lib = ctypes.CDLL(lt.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+    assert set(lt.EXPORTED) == names
+
+
+def test_status_strings():
+    assert lt.ltxattn_status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert lt.ltxattn_status_string(s) not in ("ok", "unknown status")
+    assert lt.ltxattn_status_string(7) == "unknown status"
+
+
+def test_create_rejects_before_device():
+    h = ctypes.c_void_p(1234)
+    assert lt._lib.ltxattn_create(None, ctypes.byref(h)) == lt.LTXATTN_ERR_INVALID_ARG
+    assert h.value is None
+    bad = [((0, 32, 96, 1, 16, 16), lt.LTXATTN_ERR_UNSUPPORTED),
+           ((0, 0, 128, 1, 16, 16), lt.LTXATTN_ERR_UNSUPPORTED),
+           ((0, 32, 128, 0, 16, 16), lt.LTXATTN_ERR_INVALID_ARG),
+           ((0, 32, 128, 1, 0, 16), lt.LTXATTN_ERR_INVALID_ARG),
+           ((-1, 32, 128, 1, 16, 16), lt.LTXATTN_ERR_INVALID_ARG)]
+    for args, want in bad:
+        cfg = lt.ltxattn_config(*args)
+        assert lt._lib.ltxattn_create(ctypes.byref(cfg), ctypes.byref(h)) == want, args
+    assert lt._lib.ltxattn_create(ctypes.byref(lt.ltxattn_config(0, 1, 64, 1, 1, 1)), None) \
+        == lt.LTXATTN_ERR_INVALID_ARG
+
+
+def test_null_handles():
+    io = lt.ltxattn_block_io()
+    assert lt._lib.ltxattn_block_attention(None, ctypes.byref(io), None) == lt.LTXATTN_ERR_INVALID_ARG
+    assert lt._lib.ltxattn_destroy(None) == lt.LTXATTN_OK
+    assert lt._lib.ltxattn_profile_begin(None, 4) == lt.LTXATTN_ERR_INVALID_ARG
+    assert lt._lib.ltxattn_last_hip_error(None) == 0
+
+
+# ------------------------------------------------------------ block checks
+H, D = 4, 64
+Sv, La, Lk, B = 256, 16, 13, 2
+ROW = H * D
+
+
+def _t(addr, S, sb=None, ss=ROW, sh=D):
+    return lt.ltxattn_tensor(addr, S * ROW if sb is None else sb, ss, sh)
+
+
+def make_io(**over):
+    """A valid request with fake (never dereferenced) 16-byte-aligned addresses;
+    every tensor occupies its own 1 GiB window."""
+    base = 1 << 40
+    win = 1 << 30
+    io = lt.ltxattn_block_io()
+    io.batch, io.video_len, io.audio_len, io.audio_kv_len = B, Sv, La, Lk
+    vq, vk, vv = _t(base, Sv), _t(base + win, Sv), _t(base + 2 * win, Sv)
+    aq, ak, av = _t(base + 3 * win, La), _t(base + 4 * win, La), _t(base + 5 * win, La)
+    outs = [_t(base + (6 + k) * win, Sv if k in (0, 2) else La) for k in range(4)]
+    io.attn[0] = lt.ltxattn_attn_io(vq, vk, vv, outs[0])
+    io.attn[1] = lt.ltxattn_attn_io(aq, ak, av, outs[1])
+    io.attn[2] = lt.ltxattn_attn_io(vq, ak, av, outs[2])
+    io.attn[3] = lt.ltxattn_attn_io(aq, vk, vv, outs[3])
+    for k, v in over.items():
+        setattr(io, k, v)
+    return io
+
+
+CFG = lt.ltxattn_config(0, H, D, B, Sv, La)
+
+
+def check(io, cfg=CFG):
+    return lt.ltxattn_check_block(cfg, io)
+
+
+def test_valid_request_passes():
+    assert check(make_io()) == lt.LTXATTN_OK
+    io = make_io()
+    io.attn[1].o.data = None     # skipped kind: its tensors are not looked at
+    io.attn[1].q.data = None
+    assert check(io) == lt.LTXATTN_OK
+
+
+@pytest.mark.parametrize("field,value", [
+    ("batch", 0), ("batch", B + 1), ("video_len", 0), ("video_len", Sv + 1),
+    ("audio_len", 0), ("audio_len", La + 1), ("audio_kv_len", 0), ("audio_kv_len", La + 1),
+])
+def test_sizes_out_of_range(field, value):
+    assert check(make_io(**{field: value})) == lt.LTXATTN_ERR_INVALID_ARG
+
+
+def test_audio_kv_len_equal_to_buffer_is_fine():
+    assert check(make_io(audio_kv_len=La)) == lt.LTXATTN_OK
+
+
+@pytest.mark.parametrize("kind", range(4))
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_bad_tensor(kind, which):
+    for mutate in ("null", "misaligned", "stride_s_small", "stride_odd", "stride_h_small"):
+        io = make_io()
+        t = getattr(io.attn[kind], which)
+        if mutate == "null":
+            if which == "o":
+                continue              # a null output means "skip", not an error
+            t.data = None
+        elif mutate == "misaligned":
+            t.data = t.data + 8
+        elif mutate == "stride_s_small":
+            t.stride_s = D - 8
+        elif mutate == "stride_odd":
+            t.stride_s = ROW + 4
+        elif mutate == "stride_h_small":
+            t.stride_h = 8
+        setattr(io.attn[kind], which, t)
+        assert check(io) == lt.LTXATTN_ERR_INVALID_ARG, (kind, which, mutate)
+
+
+def test_output_aliasing_rejected():
+    io = make_io()
+    o = io.attn[0].o
+    o.data = io.attn[3].k.data          # video self output on top of v2a's video K
+    io.attn[0].o = o
+    assert check(io) == lt.LTXATTN_ERR_INVALID_ARG
+    io = make_io()
+    o = io.attn[2].o
+    o.data = io.attn[0].o.data + 4096   # two outputs overlapping
+    io.attn[2].o = o
+    assert check(io) == lt.LTXATTN_ERR_INVALID_ARG
+
+
+def test_head_major_layout_accepted():
+    """[B, H, S, D] strides are a valid description of the same tensors."""
+    io = make_io()
+    for k in range(4):
+        for which in "qkvo":
+            t = getattr(io.attn[k], which)
+            S = t.stride_b // ROW
+            setattr(io.attn[k], which, lt.ltxattn_tensor(t.data, S * ROW, D, S * D))
+    assert check(io) == lt.LTXATTN_OK
+
+
+def test_unsupported_config():
+    assert check(make_io(), lt.ltxattn_config(0, H, 96, B, Sv, La)) == lt.LTXATTN_ERR_UNSUPPORTED
+    assert check(make_io(), lt.ltxattn_config(0, 0, D, B, Sv, La)) == lt.LTXATTN_ERR_UNSUPPORTED
+
+
+def test_huge_slice_unsupported():
+    """A (batch, head) slice beyond 32-bit byte offsets is refused, not mis-addressed."""
+    big = 1 << 21
+    cfg = lt.ltxattn_config(0, H, D, 1, big, La)
+    io = make_io(batch=1, video_len=big)
+    for k in (0,):
+        for which in "qkvo":
+            t = getattr(io.attn[k], which)
+            setattr(io.attn[k], which, lt.ltxattn_tensor(t.data + (k + 1) * (1 << 36) * ("qkvo".index(which) + 1),
+                                                        big * 1024, 1024, 64))
+    io.attn[1].o.data = io.attn[2].o.data = io.attn[3].o.data = None
+    assert check(io, cfg) == lt.LTXATTN_ERR_UNSUPPORTED

@@ -1,0 +1,236 @@
+"""HIP path vs the double-precision oracle, element by element, through the C ABI.
+
+* the tiny block and ragged multi-tile blocks: every output element;
+* the four full-size workloads (3840, 15360 at batch 1 and 2, 27280 video
+  tokens): sampled rows the oracle computes one by one, plus properties
+  that hold for every row (finite, inside the hull of the valid V rows, so
+  no masked poison key leaks);
+* needles at every tile / split / padding boundary, strided layouts, guard
+  bands around outputs, bit-identical reruns.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import compare, log, to_device, to_numpy
+from video_audio_diffusion_ltxattn_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ("video_self", "audio_self", "a2v", "v2a")
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _torch
+    if not _torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    return _torch
+
+
+@pytest.fixture(scope="module")
+def lt(torch):
+    # Raises (does not skip) if the HIP library is missing.
+    from video_audio_diffusion_ltxattn_amd import ltxattn
+    return ltxattn
+
+
+def run_block(lt, torch, w, inputs, kinds=KINDS):
+    log(f"  GPU block: {w.name} B{w.batch} H{w.heads} D{w.head_dim} Sv{w.video_len} "
+        f"La{w.audio_len} Lk{w.audio_kv_len} kinds={list(kinds)}")
+    dev = {n: to_device(a) for n, a in inputs.items()}
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
+    outs = ba(dev, w.audio_kv_len, kinds=kinds)
+    torch.cuda.synchronize()
+    res = {k: to_numpy(v) for k, v in outs.items()}
+    ba.close()
+    return res
+
+
+RAGGED = [
+    # several query and key tiles, ragged tails, split-KV v2a, masked audio keys
+    synth.Workload(11, "ragged D128", 2, 3, 128, 1000, 77, 70),
+    # D = 64, split v2a, one masked audio key
+    synth.Workload(12, "ragged D64", 1, 2, 64, 2100, 130, 129),
+    # a single valid audio key
+    synth.Workload(13, "one audio key", 1, 2, 64, 300, 33, 1),
+    # the smallest block
+    synth.Workload(14, "one token", 1, 1, 128, 1, 1, 1),
+    # exactly one tile everywhere, no mask
+    synth.Workload(15, "whole tiles", 1, 2, 128, 128, 64, 64),
+    # scaled keys, spike
+    synth.Workload(16, "spiky", 1, 2, 128, 700, 96, 90, k_scale=0.5, spike_rank=4, spike_amp=3.0),
+]
+
+
+@pytest.mark.parametrize("w", [synth.WORKLOADS[1]] + RAGGED, ids=lambda w: w.name)
+def test_block_full_oracle(lt, torch, w):
+    inputs = synth.make_block_inputs(w)
+    got = run_block(lt, torch, w, inputs)
+    want = oracle.block_attention(inputs, w.audio_kv_len)
+    for k in KINDS:
+        compare(got[k], want[k], f"{w.name} {k}")
+
+
+def sample_rows(rng, B, H, Sq, n_random=24):
+    special = {0, 1, 31, 32, 63, 64, 127, 128, 129, Sq - 2, Sq - 1, Sq // 2}
+    special = sorted(i for i in special if 0 <= i < Sq)
+    rows = []
+    for n, i in enumerate(special):
+        rows.append((n % B, (7 * n) % H, i))
+    for _ in range(n_random):
+        rows.append((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(Sq))))
+    return np.array(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_sampled(lt, torch, cfg):
+    w = synth.WORKLOADS[cfg]
+    inputs = synth.make_block_inputs(w)
+    got = run_block(lt, torch, w, inputs)
+    rng = np.random.default_rng(100 + cfg)
+    rows = {k: sample_rows(rng, w.batch, w.heads,
+                           w.video_len if k in ("video_self", "a2v") else w.audio_len)
+            for k in KINDS}
+    want = oracle.block_attention_rows(inputs, w.audio_kv_len, rows)
+    for k in KINDS:
+        r = rows[k]
+        compare(got[k][r[:, 0], r[:, 2], r[:, 1], :], want[k], f"cfg{cfg} {k} sampled")
+    # every row: finite and inside the hull of the valid V rows of its (b, h)
+    vv = synth.bits_to_f32(inputs["video_v"])
+    av = synth.bits_to_f32(inputs["audio_v"])[:, :w.audio_kv_len]
+    bound = {"video_self": vv, "v2a": vv, "audio_self": av, "a2v": av}
+    for k in KINDS:
+        o = got[k]
+        assert np.all(np.isfinite(o)), k
+        hi = bound[k].max(axis=1, keepdims=True) + 2e-2
+        lo = bound[k].min(axis=1, keepdims=True) - 2e-2
+        assert np.all(o <= hi) and np.all(o >= lo), f"cfg{cfg} {k}: output outside hull of valid V"
+
+
+def needle_inputs(B, H, D, Sv, La, Lk, video_pos, audio_pos, seed=7):
+    """Q = 16 e_0 everywhere; K ~ 0.25 N(0,1) with K[pos_h, h, 0] = 64 (logit 90 at
+    D = 128 for the needle), V ~ N(0,1)/16 (outputs on the scale of the real
+    workloads, so the absolute tolerance means the same).  Masked audio rows get the needle value
+    too, with V = 64: any leak of a masked key shows."""
+    rng = np.random.default_rng(seed)
+    def q(S):
+        x = np.zeros((B, S, H, D), np.float32)
+        x[..., 0] = 16.0
+        return synth.bf16_bits(x)
+    def kv(S, pos):
+        k = (0.25 * rng.standard_normal((B, S, H, D))).astype(np.float32)
+        v = (rng.standard_normal((B, S, H, D)) / 16).astype(np.float32)
+        for h in range(H):
+            k[:, pos[h % len(pos)], h, 0] = 64.0
+        return k, v
+    vk, vv = kv(Sv, video_pos)
+    ak, av = kv(La, audio_pos)
+    ak[:, Lk:, :, 0] = 64.0
+    av[:, Lk:] = 64.0
+    return {"video_q": q(Sv), "video_k": synth.bf16_bits(vk), "video_v": synth.bf16_bits(vv),
+            "audio_q": q(La), "audio_k": synth.bf16_bits(ak), "audio_v": synth.bf16_bits(av)}
+
+
+def test_needles_at_boundaries(lt, torch):
+    B, H, D, Sv, La, Lk = 1, 16, 128, 2000, 100, 90
+    # tile edges (64), query-tile edges (128), split edges of the v2a pass
+    # (2000 keys in 7 splits of 320), the last key
+    video_pos = [0, 63, 64, 127, 128, 319, 320, 639, 640, 959, 1919, 1920, 1983, 1984, 1998, 1999]
+    audio_pos = [0, 31, 32, 63, 64, 88, 89, 1]
+    inputs = needle_inputs(B, H, D, Sv, La, Lk, video_pos, audio_pos)
+    w = synth.Workload(0, "needles", B, H, D, Sv, La, Lk)
+    got = run_block(lt, torch, w, inputs)
+    rng = np.random.default_rng(9)
+    rows = {k: sample_rows(rng, B, H, Sv if k in ("video_self", "a2v") else La, n_random=40)
+            for k in KINDS}
+    # make sure every head is sampled
+    for k in KINDS:
+        extra = np.array([[0, h, (37 * h) % (Sv if k in ("video_self", "a2v") else La)]
+                          for h in range(H)], np.int64)
+        rows[k] = np.concatenate([rows[k], extra])
+    want = oracle.block_attention_rows(inputs, Lk, rows)
+    for k in KINDS:
+        r = rows[k]
+        # the needle dominates, so O ~ V[needle]: a dropped or misplaced tile is an O(1) error
+        compare(got[k][r[:, 0], r[:, 2], r[:, 1], :], want[k], f"needle {k}", guard=False)
+
+
+def test_strided_layouts_and_guard_bands(lt, torch):
+    """Inputs in [B, H, S, D] storage, outputs inside larger buffers: the
+    kernels honour every stride and write nothing outside the output view."""
+    w = synth.Workload(21, "strided", 2, 3, 128, 333, 40, 37)
+    inputs = synth.make_block_inputs(w)
+    dev = {}
+    for n, a in inputs.items():
+        t = to_device(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))   # [B, H, S, D] storage
+        dev[n] = t.permute(0, 2, 1, 3)                                 # [B, S, H, D] view
+    sentinel = 123.0
+    outs, bigs = {}, {}
+    for k in KINDS:
+        S = w.video_len if k in ("video_self", "a2v") else w.audio_len
+        big = torch.full((w.batch, S + 2, w.heads + 1, w.head_dim + 16), sentinel,
+                         dtype=torch.bfloat16, device="cuda:0")
+        bigs[k] = big
+        outs[k] = big[:, 1:S + 1, :w.heads, 8:8 + w.head_dim]
+    log("  GPU block: strided layouts + guard bands")
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
+    ba(dev, w.audio_kv_len, outs=outs)
+    torch.cuda.synchronize()
+    want = oracle.block_attention(inputs, w.audio_kv_len)
+    for k in KINDS:
+        compare(to_numpy(outs[k]), want[k], f"strided {k}")
+        big = to_numpy(bigs[k])
+        mask = np.ones(big.shape, bool)
+        mask[:, 1:-1, :w.heads, 8:8 + w.head_dim] = False
+        assert np.all(big[mask] == sentinel), f"{k}: write outside the output view"
+    ba.close()
+
+
+def test_bit_identical_reruns(lt, torch):
+    w = synth.WORKLOADS[3]
+    inputs = synth.make_block_inputs(w)
+    dev = {n: to_device(a) for n, a in inputs.items()}
+    log("  GPU block: cfg3 twice for bit identity")
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
+    o1 = ba(dev, w.audio_kv_len)
+    o1 = {k: v.clone() for k, v in o1.items()}
+    o2 = ba(dev, w.audio_kv_len)
+    torch.cuda.synchronize()
+    for k in KINDS:
+        assert torch.equal(o1[k].view(torch.int16), o2[k].view(torch.int16)), k
+    ba.close()
+
+
+def test_kinds_are_independent(lt, torch):
+    """Running a subset of kinds gives the same bits as the full block."""
+    w = RAGGED[0]
+    inputs = synth.make_block_inputs(w)
+    full = run_block(lt, torch, w, inputs)
+    for k in KINDS:
+        one = run_block(lt, torch, w, inputs, kinds=(k,))
+        assert np.array_equal(one[k], full[k]), k
+
+
+def test_profile_events(lt, torch):
+    w = synth.WORKLOADS[1]
+    dev = {n: to_device(a) for n, a in synth.make_block_inputs(w).items()}
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
+    lt.ltxattn_profile_begin(ba.handle, 4)
+    for _ in range(2):
+        ba(dev, w.audio_kv_len)
+    rec = lt.ltxattn_profile_read(ba.handle, 4)
+    lt.ltxattn_profile_end(ba.handle)
+    assert len(rec) == 2
+    for r in rec:
+        assert r["total"] > 0 and r["video_self"] > 0
+        assert r["total"] + 1e-3 >= sum(r[k] for k in KINDS)
+    ba.close()
+
+
+def test_create_on_missing_device(lt, torch):
+    cfg = lt.ltxattn_config(99, 4, 64, 1, 16, 16)
+    with pytest.raises(lt.LtxattnError) as e:
+        lt.ltxattn_create(cfg)
+    assert e.value.status == lt.LTXATTN_ERR_INVALID_ARG

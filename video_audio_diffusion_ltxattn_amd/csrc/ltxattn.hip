@@ -1,0 +1,691 @@
+// ltxattn.hip -- the per-block attention set of the LTX-2 joint video+audio
+// DiT on MI355X (gfx950): hand-written flash-attention kernels on bf16 MFMA
+// and the C ABI declared in include/ltxattn.h.
+//
+// The four attentions (video self, audio self, a2v = video Q x audio KV,
+// v2a = audio Q x video KV) are named in TensorRT-LLM PR #16228 "LTX-2:
+// replicate audio stream across Ulysses ranks by default", "Description".
+// Each computes O = softmax(Q K^T / sqrt(D)) V with bf16 inputs, fp32
+// accumulation and fp32 softmax statistics.
+//
+// Kernel design (gfx950, 64-wide waves):
+//  * A workgroup is 4 waves; each wave owns 32 query rows, so a workgroup
+//    covers BM = 128 query rows of one (batch, head).  Keys stream through
+//    in tiles of BN = 64.
+//  * Scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16: K is the A operand (from LDS) and Q^T the B
+//    operand (held in registers for the whole kernel).  In the 32x32
+//    accumulator a lane then holds ONE query (lane % 32) and 16 keys, so
+//    the online-softmax row max/sum is a per-lane loop plus one exchange
+//    between the two half-waves (v_permlane32_swap).
+//  * The output is accumulated transposed as well, O^T += V^T P^T: the
+//    probabilities P^T are the B operand straight from the score
+//    accumulators (converted to bf16 in registers, no LDS round trip) and
+//    V^T is the A operand, read from the row-major V tile in LDS with the
+//    transposing ds_read_b64_tr_b16.  Because a reduction index may be
+//    permuted freely, the key order the score accumulator happens to give
+//    each half-wave is simply used for V as well.
+//  * K and V tiles go HBM -> LDS with buffer_load ... lds (no VGPR
+//    staging), double-buffered so the next tile streams in while the
+//    current one is consumed.  Buffer range checks return zeros for rows
+//    past the valid length, which handles ragged tails and the audio key
+//    padding without branches; the padded keys are never read.
+//  * LDS rows are XOR-swizzled per tensor so the K reads (ds_read_b128, 16
+//    rows per pass) and the transposed V reads (4 rows per pass) are free
+//    of bank conflicts.
+//  * Workgroups are remapped so that each of the 8 XCDs works through a
+//    contiguous range of (batch, head) slices and the K/V of a head stay
+//    in that XCD's L2.
+//  * v2a has only La = 126..256 queries per head but 15360..27280 keys: it
+//    splits the key range over workgroups, each writing an unnormalised
+//    fp32 partial O plus its row max and row sum, and a combine kernel
+//    merges the partials by log-sum-exp in a fixed order (the same softmax
+//    statistics merge that the context-parallel v2a of TensorRT-Model-
+//    Connect PR #1586 does across ranks).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "ltxattn.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int BM = 128;          // query rows per workgroup
+constexpr int BN = 64;           // keys per tile
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int NSPLIT_MAX = 16;   // key-range splits of the v2a pass
+constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
+
+struct FaArgs {
+    const __bf16 *q, *k, *v;
+    int64_t q_sb, q_ss, q_sh;
+    int64_t k_sb, k_ss, k_sh;
+    int64_t v_sb, v_ss, v_sh;
+    __bf16 *o;
+    int64_t o_sb, o_ss, o_sh;
+    float *part_o;    // split pass: [bh][split][q_pad][D] fp32, unnormalised
+    float *part_ml;   // split pass: [bh][split][q_pad][2] = (row max * log2e/sqrt(D), row sum)
+    int B, H, Sq, kv_len;
+    int n_qtiles, nsplit, split_len, q_pad;
+    float scale_log2;  // log2(e) / sqrt(D)
+    int total;         // workgroups in the grid
+};
+
+struct CombineArgs {
+    const float *part_o, *part_ml;
+    __bf16 *o;
+    int64_t o_sb, o_ss, o_sh;
+    int B, H, Sq, nsplit, q_pad;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, RSRC_FLAGS);
+}
+
+// Swizzled 16-byte chunk of row r in an LDS tile with D bf16 per row.
+// K tiles are read 16 rows at a time at one logical chunk (ds_read_b128):
+// rotating the chunk by the row spreads those rows over all banks.  V tiles
+// are read 4 rows x 4 chunks at a time (ds_read_b64_tr_b16): each row gets
+// its own group of 4 chunks.
+template <int D> __device__ __forceinline__ int swz_k(int r, int c) {
+    constexpr int NCH = D / 8, RPB = 128 / D;
+    return c ^ ((r / RPB) % NCH);
+}
+template <int D> __device__ __forceinline__ int swz_v(int r, int c) {
+    constexpr int NCH = D / 8, RPB = 128 / D;
+    return c ^ ((4 * (r / RPB)) % NCH);
+}
+
+// Copy BN rows x D of one (batch, head) slice, starting at key row t0, from
+// HBM into an LDS tile.  Each wave instruction fills 1 KB of LDS
+// contiguously (lane i -> +16*i); the swizzle is applied by choosing which
+// global chunk each lane fetches.  Rows past the resource's range read 0.
+template <int D, bool IS_V>
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, int64_t row_stride_bytes,
+                                          int t0, char *tile, int wave, int lane) {
+    constexpr int NCH = D / 8;
+    constexpr int PER_THREAD = BN * NCH / NTHREADS;
+#pragma unroll
+    for (int n = 0; n < PER_THREAD; ++n) {
+        const int blk = n * NWAVES + wave;   // 64-chunk block filled by this wave instruction
+        const int idx = blk * 64 + lane;     // physical chunk index in the tile
+        const int r = idx / NCH, p = idx % NCH;
+        const int c = IS_V ? swz_v<D>(r, p) : swz_k<D>(r, p);  // swizzle is an involution
+        const int voff = (int)((int64_t)(t0 + r) * row_stride_bytes) + c * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(tile + blk * 1024), 16, voff, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ float xhalf_max(float x) {
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+template <int D, bool SPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(2)))
+void fa_fwd_kernel(const FaArgs a) {
+    constexpr int NCH = D / 8;
+    constexpr int KS = D / 16;       // k-steps of S^T = K Q^T
+    constexpr int NDB = D / 32;      // 32-row blocks of O^T
+    constexpr int NKB = BN / 32;     // 32-key blocks of S^T
+    constexpr int PS = BN / 16;      // k-steps of O^T += V^T P^T
+    constexpr int TILE = BN * D * 2; // bytes of one K or V tile
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // [buf 0,1] x [K, V]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hw = lane >> 5, l32 = lane & 31;
+
+    // Work item: query tile fastest, then key split, then (batch, head).
+    // Blocks are dealt to the 8 XCDs round-robin; remap so each XCD owns a
+    // contiguous range of work items (same heads -> shared K/V in its L2).
+    const int bid = blockIdx.x;
+    const int wid = (a.total % 8 == 0) ? (bid % 8) * (a.total / 8) + bid / 8 : bid;
+    const int qt = wid % a.n_qtiles;
+    const int rest = wid / a.n_qtiles;
+    const int split = rest % a.nsplit;
+    const int bh = rest / a.nsplit;
+    const int b = bh / a.H, hh = bh % a.H;
+
+    const int kv_begin = split * a.split_len;
+    const int kv_end = min(a.kv_len, kv_begin + a.split_len);
+    const float c = a.scale_log2;
+
+    const __bf16 *qb = a.q + b * a.q_sb + hh * a.q_sh;
+    const __bf16 *kb = a.k + b * a.k_sb + hh * a.k_sh;
+    const __bf16 *vb = a.v + b * a.v_sb + hh * a.v_sh;
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qb, ((int64_t)(a.Sq - 1) * a.q_ss + D) * 2);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, ((int64_t)(a.kv_len - 1) * a.k_ss + D) * 2);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, ((int64_t)(a.kv_len - 1) * a.v_ss + D) * 2);
+
+    // Start streaming the first K/V tile before touching Q.
+    load_tile<D, false>(kr, a.k_ss * 2, kv_begin, smem, wave, lane);
+    load_tile<D, true>(vr, a.v_ss * 2, kv_begin, smem + TILE, wave, lane);
+
+    // Q^T as the B operand: lane holds 8 consecutive d of its query row per k-step.
+    const int qrow = qt * BM + wave * 32 + l32;
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(qr, (int)((int64_t)qrow * a.q_ss * 2) + (2 * s + hw) * 16, 0, 0);
+        qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    f32x16 acc_o[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) acc_o[i] = f32x16{};
+    float m_run = -1e30f;   // running row max of the raw scores (finite start: no inf - inf)
+    float l_run = 0.f;      // this half-wave's share of the running row sum
+
+    const int ntiles = (kv_end - kv_begin + BN - 1) / BN;
+    for (int t = 0; t < ntiles; ++t) {
+        const int t0 = kv_begin + t * BN;
+        char *ktile = smem + (t & 1) * 2 * TILE;
+        char *vtile = ktile + TILE;
+        // Tile t has landed (own loads) and every wave is done with the other buffer.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t + 1 < ntiles) {
+            char *nk = smem + ((t + 1) & 1) * 2 * TILE;
+            load_tile<D, false>(kr, a.k_ss * 2, t0 + BN, nk, wave, lane);
+            load_tile<D, true>(vr, a.v_ss * 2, t0 + BN, nk + TILE, wave, lane);
+        }
+
+        // S^T = K Q^T: acc_s[kb][i*4+j] is the score of key t0 + 32kb + 8i + 4hw + j
+        // against query qrow.
+        f32x16 acc_s[NKB];
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2) {
+            acc_s[kb2] = f32x16{};
+            const int r = 32 * kb2 + l32;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int p = swz_k<D>(r, 2 * s + hw);
+                const u32x4 w = *(const LDS_AS u32x4 *)((LDS_AS char *)ktile + r * (2 * D) + p * 16);
+                acc_s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), qf[s],
+                                                                     acc_s[kb2], 0, 0, 0);
+            }
+        }
+
+        // Keys at or past kv_end (ragged tail, audio padding) get -inf.
+        if (t0 + BN > kv_end) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = t0 + 32 * kb2 + 8 * (e >> 2) + 4 * hw + (e & 3);
+                    if (key >= kv_end) acc_s[kb2][e] = -INFINITY;
+                }
+        }
+
+        // Online softmax in the exp2 domain.
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc_s[kb2][e]);
+        mx = xhalf_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        m_run = m_new;
+        const float mc = m_new * c;
+        float rs = 0.f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(fmaf(acc_s[kb2][e], c, -mc));
+                acc_s[kb2][e] = pe;
+                rs += pe;
+            }
+        l_run = l_run * alpha + rs;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc_o[db][e] *= alpha;
+
+        // O^T += V^T P^T.  k-step s covers keys 16s..16s+15 of the tile; this
+        // half-wave contributes keys 16s + 4hw + {0..3} and 16s + 8 + 4hw + {0..3}.
+#pragma unroll
+        for (int s = 0; s < PS; ++s) {
+            const int kb2 = s >> 1, i0 = 2 * (s & 1);
+            bf16x8 pf;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pf[j] = (__bf16)acc_s[kb2][i0 * 4 + j];
+                pf[4 + j] = (__bf16)acc_s[kb2][(i0 + 1) * 4 + j];
+            }
+            const int li = lane & 15, g = (lane >> 4) & 1;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int col = 32 * db + 16 * g + 4 * (li & 3);
+                const int cch = col >> 3, half = (col >> 2) & 1;
+                const int r0 = 16 * s + 4 * hw + (li >> 2);
+                const int r1 = r0 + 8;
+                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (LDS_AS i16x4 *)((LDS_AS char *)vtile + r0 * (2 * D) + swz_v<D>(r0, cch) * 16 + half * 8));
+                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (LDS_AS i16x4 *)((LDS_AS char *)vtile + r1 * (2 * D) + swz_v<D>(r1, cch) * 16 + half * 8));
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc_o[db], 0, 0, 0);
+            }
+        }
+    }
+
+    // acc_o[db][i*4+j] is O^T[d = 32db + 8i + 4hw + j][query qrow] (unnormalised).
+    const float l_tot = xhalf_sum(l_run);
+    if (!SPLIT) {
+        if (qrow < a.Sq) {
+            const float inv = 1.0f / l_tot;
+            __bf16 *orow = a.o + b * a.o_sb + (int64_t)qrow * a.o_ss + hh * a.o_sh;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bf16x4 ov;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(acc_o[db][i * 4 + j] * inv);
+                    *(bf16x4 *)(orow + 32 * db + 8 * i + 4 * hw) = ov;
+                }
+        }
+    } else {
+        const int64_t prow = ((int64_t)bh * a.nsplit + split) * a.q_pad + qrow;
+        float *po = a.part_o + prow * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 ov;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ov[j] = acc_o[db][i * 4 + j];
+                *(f32x4 *)(po + 32 * db + 8 * i + 4 * hw) = ov;
+            }
+        if (hw == 0) {
+            a.part_ml[prow * 2 + 0] = m_run * c;
+            a.part_ml[prow * 2 + 1] = l_tot;
+        }
+    }
+}
+
+// Merge the split partials of one output row: M = max_r m_r,
+// L = sum_r l_r 2^(m_r - M), O = sum_r 2^(m_r - M) O_r / L, in split order.
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void fa_combine_kernel(const CombineArgs a) {
+    constexpr int TPR = D / 4;   // threads per output row, 4 floats each
+    const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gt / TPR;
+    const int d4 = (int)(gt % TPR);
+    if (row >= (int64_t)a.B * a.H * a.Sq) return;
+    const int q = (int)(row % a.Sq);
+    const int bh = (int)(row / a.Sq);
+    const int b = bh / a.H, hh = bh % a.H;
+    const int64_t base = (int64_t)bh * a.nsplit * a.q_pad + q;
+    float M = -INFINITY;
+    for (int r = 0; r < a.nsplit; ++r) M = fmaxf(M, a.part_ml[(base + (int64_t)r * a.q_pad) * 2]);
+    float L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < a.nsplit; ++r) {
+        const int64_t pr = base + (int64_t)r * a.q_pad;
+        const float w = __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - M);
+        L += w * a.part_ml[pr * 2 + 1];
+        const f32x4 ov = *(const f32x4 *)(a.part_o + pr * D + d4 * 4);
+        acc += w * ov;
+    }
+    const float inv = 1.0f / L;
+    bf16x4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = (__bf16)(acc[j] * inv);
+    *(bf16x4 *)(a.o + b * a.o_sb + (int64_t)q * a.o_ss + hh * a.o_sh + d4 * 4) = out;
+}
+
+// ------------------------------------------------------------------ host side
+
+struct Extent {
+    uintptr_t lo, hi;
+};
+
+int check_tensor(const ltxattn_tensor &t, int B, int S, int H, int D, Extent *ext) {
+    if (!t.data) return LTXATTN_ERR_INVALID_ARG;
+    if ((uintptr_t)t.data % 16) return LTXATTN_ERR_INVALID_ARG;
+    if (t.stride_b < 0 || t.stride_s < D || t.stride_h < D) return LTXATTN_ERR_INVALID_ARG;
+    if (t.stride_b % 8 || t.stride_s % 8 || t.stride_h % 8) return LTXATTN_ERR_INVALID_ARG;
+    // One (batch, head) slice, plus the rows a kernel may touch past the end
+    // of it (a query tile and a key tile), must be addressable with 32-bit
+    // byte offsets, so that buffer range checks see every such row.
+    const int64_t slice = ((int64_t)(S + BM + BN) * t.stride_s + D) * 2;
+    if (slice >= ((int64_t)1 << 31) - 64) return LTXATTN_ERR_UNSUPPORTED;
+    const int64_t span = (int64_t)(B - 1) * t.stride_b + (int64_t)(S - 1) * t.stride_s +
+                         (int64_t)(H - 1) * t.stride_h + D;
+    ext->lo = (uintptr_t)t.data;
+    ext->hi = (uintptr_t)t.data + (uintptr_t)span * 2;
+    return LTXATTN_OK;
+}
+
+bool overlaps(const Extent &x, const Extent &y) { return x.lo < y.hi && y.lo < x.hi; }
+
+}  // namespace
+
+struct ltxattn_handle {
+    int device;
+    int heads, head_dim, max_batch, max_video_len, max_audio_len;
+    int num_cus;
+    float *ws_o;
+    float *ws_ml;
+    int64_t ws_rows;
+    int last_hip_error;
+    // profiling
+    hipEvent_t *events;
+    int prof_max, prof_n;
+};
+
+namespace {
+
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev) {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) {
+            err = hipSetDevice(dev);
+            changed = (err == hipSuccess);
+        }
+    }
+    ~DeviceGuard() {
+        if (changed) (void)hipSetDevice(prev);
+    }
+};
+
+// hipError_t of the last failed ltxattn_create on this thread (no handle to keep it in).
+thread_local int g_create_hip_error = 0;
+
+int hip_fail(ltxattn_handle *h, hipError_t e) {
+    if (h) h->last_hip_error = (int)e;
+    return LTXATTN_ERR_HIP;
+}
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// How many key-range splits the v2a pass uses: enough workgroups to give
+// every CU two, at least four key tiles per split, at most NSPLIT_MAX.
+int choose_nsplit(int base_wgs, int kv_len, int num_cus) {
+    int ns = ceil_div(2 * num_cus, base_wgs);
+    ns = ns < NSPLIT_MAX ? ns : NSPLIT_MAX;
+    const int by_len = kv_len / (4 * BN);
+    ns = ns < by_len ? ns : by_len;
+    return ns < 1 ? 1 : ns;
+}
+
+int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len,
+                  bool allow_split, hipStream_t st) {
+    const int D = h->head_dim, H = h->heads;
+    FaArgs a;
+    a.q = (const __bf16 *)io.q.data;
+    a.k = (const __bf16 *)io.k.data;
+    a.v = (const __bf16 *)io.v.data;
+    a.q_sb = io.q.stride_b; a.q_ss = io.q.stride_s; a.q_sh = io.q.stride_h;
+    a.k_sb = io.k.stride_b; a.k_ss = io.k.stride_s; a.k_sh = io.k.stride_h;
+    a.v_sb = io.v.stride_b; a.v_ss = io.v.stride_s; a.v_sh = io.v.stride_h;
+    a.o = (__bf16 *)io.o.data;
+    a.o_sb = io.o.stride_b; a.o_ss = io.o.stride_s; a.o_sh = io.o.stride_h;
+    a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
+    a.n_qtiles = ceil_div(Sq, BM);
+    a.q_pad = a.n_qtiles * BM;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    const int base = B * H * a.n_qtiles;
+    int ns = allow_split ? choose_nsplit(base, kv_len, h->num_cus) : 1;
+    a.split_len = ceil_div(ceil_div(kv_len, ns), BN) * BN;
+    ns = ceil_div(kv_len, a.split_len);
+    a.nsplit = ns;
+    a.part_o = h->ws_o;
+    a.part_ml = h->ws_ml;
+    a.total = base * ns;
+    const bool split = ns > 1;
+    if (split && (int64_t)base * ns * BM > h->ws_rows) return LTXATTN_ERR_INVALID_ARG;  // cannot happen
+
+    if (D == 128) {
+        if (split) hipLaunchKernelGGL((fa_fwd_kernel<128, true>), dim3(a.total), dim3(NTHREADS), 0, st, a);
+        else hipLaunchKernelGGL((fa_fwd_kernel<128, false>), dim3(a.total), dim3(NTHREADS), 0, st, a);
+    } else {
+        if (split) hipLaunchKernelGGL((fa_fwd_kernel<64, true>), dim3(a.total), dim3(NTHREADS), 0, st, a);
+        else hipLaunchKernelGGL((fa_fwd_kernel<64, false>), dim3(a.total), dim3(NTHREADS), 0, st, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(h, e);
+    if (split) {
+        CombineArgs c;
+        c.part_o = h->ws_o; c.part_ml = h->ws_ml;
+        c.o = a.o; c.o_sb = a.o_sb; c.o_ss = a.o_ss; c.o_sh = a.o_sh;
+        c.B = B; c.H = H; c.Sq = Sq; c.nsplit = ns; c.q_pad = a.q_pad;
+        const int64_t threads = (int64_t)B * H * Sq * (D / 4);
+        const int grid = ceil_div(threads, 256);
+        if (D == 128) hipLaunchKernelGGL((fa_combine_kernel<128>), dim3(grid), dim3(256), 0, st, c);
+        else hipLaunchKernelGGL((fa_combine_kernel<64>), dim3(grid), dim3(256), 0, st, c);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(h, e);
+    }
+    return LTXATTN_OK;
+}
+
+// Argument checks shared by ltxattn_check_block and ltxattn_block_attention.
+// on[k] is set for the kinds whose output pointer is non-null.
+int validate_block(const ltxattn_config &caps, const ltxattn_block_io *io, bool on[4]) {
+    const int B = io->batch, Sv = io->video_len, La = io->audio_len, Lk = io->audio_kv_len;
+    if (B < 1 || B > caps.max_batch) return LTXATTN_ERR_INVALID_ARG;
+    if (Sv < 1 || Sv > caps.max_video_len) return LTXATTN_ERR_INVALID_ARG;
+    if (La < 1 || La > caps.max_audio_len) return LTXATTN_ERR_INVALID_ARG;
+    if (Lk < 1 || Lk > La) return LTXATTN_ERR_INVALID_ARG;
+    const int H = caps.heads, D = caps.head_dim;
+    // Rows of q/o and of k/v per kind.
+    const int q_rows[4] = {Sv, La, Sv, La};
+    const int kv_rows[4] = {Sv, La, La, Sv};
+    Extent in_ext[4][3], out_ext[4];
+    for (int k = 0; k < 4; ++k) {
+        const ltxattn_attn_io &x = io->attn[k];
+        on[k] = x.o.data != nullptr;
+        if (!on[k]) continue;
+        int rc;
+        if ((rc = check_tensor(x.q, B, q_rows[k], H, D, &in_ext[k][0]))) return rc;
+        if ((rc = check_tensor(x.k, B, kv_rows[k], H, D, &in_ext[k][1]))) return rc;
+        if ((rc = check_tensor(x.v, B, kv_rows[k], H, D, &in_ext[k][2]))) return rc;
+        if ((rc = check_tensor(x.o, B, q_rows[k], H, D, &out_ext[k]))) return rc;
+    }
+    for (int k = 0; k < 4; ++k) {
+        if (!on[k]) continue;
+        for (int j = 0; j < 4; ++j) {
+            if (!on[j]) continue;
+            for (int t = 0; t < 3; ++t)
+                if (overlaps(out_ext[k], in_ext[j][t])) return LTXATTN_ERR_INVALID_ARG;
+            if (j != k && overlaps(out_ext[k], out_ext[j])) return LTXATTN_ERR_INVALID_ARG;
+        }
+    }
+    return LTXATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ltxattn_status_string(int status) {
+    switch (status) {
+        case LTXATTN_OK: return "ok";
+        case LTXATTN_ERR_INVALID_ARG: return "invalid argument";
+        case LTXATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case LTXATTN_ERR_HIP: return "HIP runtime error";
+        case LTXATTN_ERR_OOM: return "device workspace allocation failed";
+        default: return "unknown status";
+    }
+}
+
+int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
+    if (!out) return LTXATTN_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!cfg) return LTXATTN_ERR_INVALID_ARG;
+    if (cfg->head_dim != 64 && cfg->head_dim != 128) return LTXATTN_ERR_UNSUPPORTED;
+    if (cfg->heads < 1) return LTXATTN_ERR_UNSUPPORTED;
+    if (cfg->max_batch < 1 || cfg->max_video_len < 1 || cfg->max_audio_len < 1 || cfg->device < 0)
+        return LTXATTN_ERR_INVALID_ARG;
+    int ndev = 0;
+    hipError_t e = hipGetDeviceCount(&ndev);
+    if (e != hipSuccess) { g_create_hip_error = (int)e; return LTXATTN_ERR_HIP; }
+    if (cfg->device >= ndev) return LTXATTN_ERR_INVALID_ARG;
+
+    ltxattn_handle *h = (ltxattn_handle *)calloc(1, sizeof(ltxattn_handle));
+    if (!h) return LTXATTN_ERR_OOM;
+    h->device = cfg->device;
+    h->heads = cfg->heads;
+    h->head_dim = cfg->head_dim;
+    h->max_batch = cfg->max_batch;
+    h->max_video_len = cfg->max_video_len;
+    h->max_audio_len = cfg->max_audio_len;
+
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) { g_create_hip_error = (int)g.err; free(h); return LTXATTN_ERR_HIP; }
+    e = hipDeviceGetAttribute(&h->num_cus, hipDeviceAttributeMultiprocessorCount, h->device);
+    if (e != hipSuccess) { g_create_hip_error = (int)e; free(h); return LTXATTN_ERR_HIP; }
+    // Workspace of the v2a split pass: every (batch, head, query tile) times the
+    // largest split count, rows padded to whole query tiles.
+    h->ws_rows = (int64_t)h->max_batch * h->heads * ceil_div(h->max_audio_len, BM) * BM * NSPLIT_MAX;
+    e = hipMalloc((void **)&h->ws_o, (size_t)h->ws_rows * h->head_dim * sizeof(float));
+    if (e != hipSuccess) { g_create_hip_error = (int)e; (void)hipGetLastError(); free(h); return LTXATTN_ERR_OOM; }
+    e = hipMalloc((void **)&h->ws_ml, (size_t)h->ws_rows * 2 * sizeof(float));
+    if (e != hipSuccess) {
+        g_create_hip_error = (int)e;
+        (void)hipGetLastError();
+        (void)hipFree(h->ws_o);
+        free(h);
+        return LTXATTN_ERR_OOM;
+    }
+    *out = h;
+    return LTXATTN_OK;
+}
+
+int ltxattn_destroy(ltxattn_handle *h) {
+    if (!h) return LTXATTN_OK;
+    DeviceGuard g(h->device);
+    if (h->events) ltxattn_profile_end(h);
+    hipError_t e1 = hipFree(h->ws_o);
+    hipError_t e2 = hipFree(h->ws_ml);
+    free(h);
+    return (e1 == hipSuccess && e2 == hipSuccess) ? LTXATTN_OK : LTXATTN_ERR_HIP;
+}
+
+int ltxattn_last_hip_error(const ltxattn_handle *h) { return h ? h->last_hip_error : g_create_hip_error; }
+
+int ltxattn_check_block(const ltxattn_config *cfg, const ltxattn_block_io *io) {
+    if (!cfg || !io) return LTXATTN_ERR_INVALID_ARG;
+    if (cfg->head_dim != 64 && cfg->head_dim != 128) return LTXATTN_ERR_UNSUPPORTED;
+    if (cfg->heads < 1) return LTXATTN_ERR_UNSUPPORTED;
+    bool on[4];
+    return validate_block(*cfg, io, on);
+}
+
+int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void *hip_stream) {
+    if (!h || !io) return LTXATTN_ERR_INVALID_ARG;
+    const ltxattn_config caps = {h->device, h->heads, h->head_dim, h->max_batch, h->max_video_len,
+                                 h->max_audio_len};
+    bool on[4];
+    const int vrc = validate_block(caps, io, on);
+    if (vrc) return vrc;
+    const int B = io->batch, Sv = io->video_len, La = io->audio_len, Lk = io->audio_kv_len;
+    const int q_rows[4] = {Sv, La, Sv, La};
+
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return hip_fail(h, g.err);
+    hipStream_t st = (hipStream_t)hip_stream;
+    hipEvent_t *ev = nullptr;
+    if (h->events && h->prof_n < h->prof_max) ev = h->events + (int64_t)h->prof_n++ * 5;
+    hipError_t e;
+    if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail(h, e);
+
+    // Fixed order: video self, a2v, v2a, audio self.  Event slot k+1 closes kind order[k].
+    const int order[4] = {LTXATTN_VIDEO_SELF, LTXATTN_A2V, LTXATTN_V2A, LTXATTN_AUDIO_SELF};
+    for (int n = 0; n < 4; ++n) {
+        const int k = order[n];
+        if (on[k]) {
+            const int kv_len = (k == LTXATTN_AUDIO_SELF || k == LTXATTN_A2V) ? Lk : Sv;
+            const int rc = run_attention(h, io->attn[k], B, q_rows[k], kv_len, k == LTXATTN_V2A, st);
+            if (rc) return rc;
+        }
+        if (ev && (e = hipEventRecord(ev[n + 1], st)) != hipSuccess) return hip_fail(h, e);
+    }
+    return LTXATTN_OK;
+}
+
+int ltxattn_profile_begin(ltxattn_handle *h, int32_t max_calls) {
+    if (!h || max_calls < 1) return LTXATTN_ERR_INVALID_ARG;
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return hip_fail(h, g.err);
+    if (h->events) ltxattn_profile_end(h);
+    h->events = (hipEvent_t *)calloc((size_t)max_calls * 5, sizeof(hipEvent_t));
+    if (!h->events) return LTXATTN_ERR_OOM;
+    for (int64_t i = 0; i < (int64_t)max_calls * 5; ++i) {
+        hipError_t e = hipEventCreate(&h->events[i]);
+        if (e != hipSuccess) {
+            for (int64_t j = 0; j < i; ++j) (void)hipEventDestroy(h->events[j]);
+            free(h->events);
+            h->events = nullptr;
+            return hip_fail(h, e);
+        }
+    }
+    h->prof_max = max_calls;
+    h->prof_n = 0;
+    return LTXATTN_OK;
+}
+
+int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_t *n_calls) {
+    if (!h || !ms || !n_calls || max_calls < 1 || !h->events) return LTXATTN_ERR_INVALID_ARG;
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return hip_fail(h, g.err);
+    const int n = h->prof_n < max_calls ? h->prof_n : max_calls;
+    // Slot n+1 of a call closes kind order[n] (video self, a2v, v2a, audio self).
+    const int kind_of_slot[4] = {LTXATTN_VIDEO_SELF, LTXATTN_A2V, LTXATTN_V2A, LTXATTN_AUDIO_SELF};
+    for (int c = 0; c < n; ++c) {
+        hipEvent_t *ev = h->events + (int64_t)c * 5;
+        hipError_t e = hipEventSynchronize(ev[4]);
+        if (e != hipSuccess) return hip_fail(h, e);
+        for (int s = 0; s < 4; ++s) {
+            float t = 0.f;
+            e = hipEventElapsedTime(&t, ev[s], ev[s + 1]);
+            if (e != hipSuccess) return hip_fail(h, e);
+            ms[c * 5 + kind_of_slot[s]] = t;
+        }
+        float tot = 0.f;
+        e = hipEventElapsedTime(&tot, ev[0], ev[4]);
+        if (e != hipSuccess) return hip_fail(h, e);
+        ms[c * 5 + 4] = tot;
+    }
+    *n_calls = n;
+    return LTXATTN_OK;
+}
+
+int ltxattn_profile_end(ltxattn_handle *h) {
+    if (!h) return LTXATTN_ERR_INVALID_ARG;
+    if (!h->events) return LTXATTN_OK;
+    DeviceGuard g(h->device);
+    for (int64_t i = 0; i < (int64_t)h->prof_max * 5; ++i) (void)hipEventDestroy(h->events[i]);
+    free(h->events);
+    h->events = nullptr;
+    h->prof_max = h->prof_n = 0;
+    return LTXATTN_OK;
+}
+
+}  // extern "C"
