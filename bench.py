@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Benchmark: attention TFLOP/s of one LTX-2 DiT block's attention set on one MI355X.
+
+A step is one ``ltxattn_block_attention`` call -- video self-attention, a2v,
+v2a (split-KV pass + combine) and audio self-attention -- over the
+768x1280x121 clip: 15360 video tokens, 126 audio tokens padded to 128, 32
+heads of 128, batch 1 (TensorRT-LLM PR #16228, "Description").  Inputs are
+seeded synthetic bf16 tensors already resident in HBM.
+
+Prints one JSON line.  ``value`` is the block's algorithmic attention FLOPs
+(4*B*H*Sq*Sk_valid*D summed over the four kinds) per second of step time.
+``roofline`` describes the dominant kernel (video self-attention), timed
+with HIP events the library records on the stream it launches on.
+``cpu_baseline`` is the double-precision oracle on a bounded sample of the
+same work on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from video_audio_diffusion_ltxattn_amd import synth  # noqa: E402
+
+METRIC = "attention TFLOP/s + % bf16 MFMA peak per DiT block (15360 video/126 audio tok)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KINDS = ("video_self", "audio_self", "a2v", "v2a")
+KERNEL_SRC = os.path.join(ROOT, "video_audio_diffusion_ltxattn_amd", "csrc", "ltxattn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_video_self_15360.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per video-self launch from the committed rocprofv3 counter
+    runs, or None if they were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(inputs: dict, w: synth.Workload, min_s: float, max_s: float) -> dict:
+    """The oracle, as it stands, on video self-attention rows of the same inputs:
+    whole rows (all keys), in chunks, until at least min_s seconds have passed."""
+    import oracle
+    threads = oracle.default_threads()
+    q, k, v = inputs["video_q"], inputs["video_k"], inputs["video_v"]
+    rng = np.random.default_rng(0)
+    chunk = 8 * threads
+    rows_done = 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    while elapsed < min_s:
+        rows = np.stack([rng.integers(0, w.batch, chunk), rng.integers(0, w.heads, chunk),
+                         rng.integers(0, w.video_len, chunk)], axis=1)
+        oracle.attention_rows(q, k, v, rows, threads=threads)
+        rows_done += chunk
+        elapsed = time.perf_counter() - t0
+        if elapsed > max_s:
+            break
+    flops = 4.0 * rows_done * w.video_len * w.head_dim
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{rows_done} random video self-attention query rows of the block workload "
+                   f"(each over all {w.video_len} keys, D={w.head_dim}), double precision, "
+                   f"{elapsed:.1f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cfg", type=int, default=3, help="workload (1..5); 3 is the headline block")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(no sharding, no collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from video_audio_diffusion_ltxattn_amd import ltxattn as lt
+
+    w = synth.WORKLOADS[args.cfg]
+    inputs = synth.make_block_inputs(w)
+    dev = {}
+    for n, a in inputs.items():
+        dev[n] = torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to("cuda:0")
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
+    outs = {k: torch.empty_like(dev["video_q"] if k in ("video_self", "a2v") else dev["audio_q"])
+            for k in KINDS}
+    stream = torch.cuda.current_stream()
+    io = ba.make_io(dev, w.audio_kv_len, outs)
+
+    for _ in range(args.warmup):
+        lt.ltxattn_block_attention(ba.handle, io, stream.cuda_stream)
+    torch.cuda.synchronize()
+
+    lt.ltxattn_profile_begin(ba.handle, args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        lt.ltxattn_block_attention(ba.handle, io, stream.cuda_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rec = lt.ltxattn_profile_read(ba.handle, args.steps)
+    lt.ltxattn_profile_end(ba.handle)
+
+    for k in KINDS:
+        assert torch.isfinite(outs[k].float()).all(), f"{k}: non-finite output"
+
+    flops = synth.attention_flops(w)
+    nbytes = synth.attention_bytes(w)
+    ms_step = wall * 1e3 / args.steps
+    value = sum(flops.values()) / (ms_step * 1e-3) / 1e12
+    kind_ms = {k: float(np.mean([r[k] for r in rec])) for k in KINDS}
+    kinds = {}
+    for k in KINDS:
+        t = kind_ms[k] * 1e-3
+        kinds[k] = {"ms": round(kind_ms[k], 5),
+                    "tflops": round(flops[k] / t / 1e12, 2),
+                    "pct_bf16_peak": round(100 * flops[k] / t / 1e12 / PEAK_BF16_TFLOPS, 2),
+                    "hbm_gbs": round(nbytes[k] / t / 1e9, 1),
+                    "pct_hbm_peak": round(100 * nbytes[k] / t / 1e9 / PEAK_HBM_GBS, 2)}
+    vs_ms = kind_ms["video_self"]
+    achieved = flops["video_self"] / (vs_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, masked audio keys poisoned)",
+        "config": {"workload": f"LTX-2 block attention set, {w.name}",
+                   "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+                   "video_tokens": w.video_len, "audio_tokens": w.audio_kv_len,
+                   "audio_buffer_rows": w.audio_len, "parallelism": "none (1 GPU)"},
+        "kinds": kinds,
+        "roofline": {"kernel": "fa_fwd_kernel<128,false> (video self-attention)",
+                     "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(),
+                     "avg_launch_ms": round(vs_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inputs, w, args.cpu_seconds, 3 * args.cpu_seconds)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)
+    print(json.dumps(out), flush=True)
+    ba.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -26,10 +26,10 @@
 //    permuted freely, the key order the score accumulator happens to give
 //    each half-wave is simply used for V as well.
 //  * K and V tiles go HBM -> LDS with buffer_load ... lds (no VGPR
-//    staging), double-buffered so the next tile streams in while the
-//    current one is consumed.  Buffer range checks return zeros for rows
-//    past the valid length, which handles ragged tails and the audio key
-//    padding without branches; the padded keys are never read.
+//    staging), double-buffered: the next tile streams in while the current
+//    one is consumed.  Buffer range checks return zeros for rows past the
+//    valid length, which handles ragged tails and the audio key padding
+//    without branches; the padded keys are never read.
 //  * LDS rows are XOR-swizzled per tensor so the K reads (ds_read_b128, 16
 //    rows per pass) and the transposed V reads (4 rows per pass) are free
 //    of bank conflicts.
@@ -55,6 +55,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -109,24 +110,29 @@ template <int D> __device__ __forceinline__ int swz_v(int r, int c) {
     return c ^ ((4 * (r / RPB)) % NCH);
 }
 
+// Per-lane byte offsets that do not change from tile to tile.
+template <int D>
+struct LaneOffsets {
+    static constexpr int KS = D / 16, NDB = D / 32;
+    static constexpr int PER_THREAD = BN * (D / 8) / NTHREADS;   // DMA chunks per thread per tile
+    int k_rd[KS];          // K tile, ds_read_b128 for k-step s (key block 0; block 1 is +32 rows)
+    int v_rd[NDB];         // V tile, ds_read_b64_tr_b16 for d block db (k-step s adds 16s rows)
+    int k_src[PER_THREAD]; // global byte offset (minus the tile's first row) of each K chunk
+    int v_src[PER_THREAD];
+};
+
 // Copy BN rows x D of one (batch, head) slice, starting at key row t0, from
-// HBM into an LDS tile.  Each wave instruction fills 1 KB of LDS
-// contiguously (lane i -> +16*i); the swizzle is applied by choosing which
-// global chunk each lane fetches.  Rows past the resource's range read 0.
-template <int D, bool IS_V>
-__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, int64_t row_stride_bytes,
-                                          int t0, char *tile, int wave, int lane) {
-    constexpr int NCH = D / 8;
-    constexpr int PER_THREAD = BN * NCH / NTHREADS;
+// HBM into an LDS tile with buffer_load ... lds.  Each wave instruction
+// fills 1 KB of LDS contiguously (lane i -> +16*i); the swizzle is applied by
+// choosing which global chunk each lane fetches (src).  Rows past the
+// resource's range read as zeros.
+template <int D>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rsrc, const int *src, int soff,
+                                         LDS_AS char *tile, int wave) {
 #pragma unroll
-    for (int n = 0; n < PER_THREAD; ++n) {
-        const int blk = n * NWAVES + wave;   // 64-chunk block filled by this wave instruction
-        const int idx = blk * 64 + lane;     // physical chunk index in the tile
-        const int r = idx / NCH, p = idx % NCH;
-        const int c = IS_V ? swz_v<D>(r, p) : swz_k<D>(r, p);  // swizzle is an involution
-        const int voff = (int)((int64_t)(t0 + r) * row_stride_bytes) + c * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(tile + blk * 1024), 16, voff, 0, 0, 0);
-    }
+    for (int n = 0; n < LaneOffsets<D>::PER_THREAD; ++n)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(tile + (n * NWAVES + wave) * 1024), 16,
+                                                 src[n], soff, 0, 0);
 }
 
 __device__ __forceinline__ float xhalf_max(float x) {
@@ -138,16 +144,142 @@ __device__ __forceinline__ float xhalf_sum(float x) {
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// Wait for all of this wave's outstanding memory loads (including DMA into
+// LDS), then synchronise the workgroup.
+__device__ __forceinline__ void tile_barrier() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+}
+
+// Rescaling of the running output is skipped until some row's max has grown
+// by more than 2^RESCALE_LOG2 over the max in use: until then probabilities
+// are taken against the stale max and stay below 2^RESCALE_LOG2.  Exact
+// algebra: O / l does not depend on which max was subtracted.
+constexpr float RESCALE_LOG2 = 8.0f;
+
+template <int D>
+struct RowState {
+    f32x16 o[D / 32];   // O^T accumulator: o[db][i*4+j] = O^T[32db + 8i + 4hw + j][query]
+    float m;            // max in use (raw score units)
+    float l;            // this half-wave's share of the row sum
+};
+
+struct TileCtx {
+    __amdgpu_buffer_rsrc_t kr, vr;
+    int k_stride, v_stride;   // bytes per key row
+    int kv_end;
+    float c;                  // log2(e) / sqrt(D)
+    int wave, hw;
+};
+
+// One key tile: prefetch the next tile into the other buffer, then
+// S^T = K Q^T, online softmax, O^T += V^T P^T.  The LDS tiles are passed as
+// restrict pointers: the compiler can then tell that the reads of this tile
+// do not touch the buffer the prefetch is writing, and does not wait for it.
+template <int D>
+__device__ __forceinline__ void attend_tile(const TileCtx &x, const LaneOffsets<D> &lo, const bf16x8 *qf,
+                                            RowState<D> &st, int t0, bool prefetch,
+                                            const LDS_AS char *__restrict__ kcur,
+                                            const LDS_AS char *__restrict__ vcur,
+                                            LDS_AS char *__restrict__ knext,
+                                            LDS_AS char *__restrict__ vnext) {
+    constexpr int KS = D / 16, NDB = D / 32, NKB = BN / 32, PS = BN / 16;
+    if (prefetch) {
+        dma_tile<D>(x.kr, lo.k_src, (t0 + BN) * x.k_stride, knext, x.wave);
+        dma_tile<D>(x.vr, lo.v_src, (t0 + BN) * x.v_stride, vnext, x.wave);
+    }
+
+    // S^T = K Q^T: s[kb][i*4+j] = score of key t0 + 32kb + 8i + 4hw + j against this lane's query.
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const u32x4 w = *(const LDS_AS u32x4 *)(kcur + kb * 32 * 2 * D + lo.k_rd[k]);
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), qf[k], s[kb], 0, 0, 0);
+        }
+    }
+
+    // Keys at or past kv_end (ragged tail, audio padding) get -inf.
+    if (t0 + BN > x.kv_end) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int key = t0 + 32 * kb + 8 * (e >> 2) + 4 * x.hw + (e & 3);
+                if (key >= x.kv_end) s[kb][e] = -INFINITY;
+            }
+    }
+
+    // Row max: two independent chains, then the other half-wave.
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; e += 4) {
+            mx0 = fmaxf(fmaxf(mx0, s[kb][e]), s[kb][e + 1]);        // v_max3
+            mx1 = fmaxf(fmaxf(mx1, s[kb][e + 2]), s[kb][e + 3]);
+        }
+    const float mx = xhalf_max(fmaxf(mx0, mx1));
+    if (__builtin_amdgcn_ballot_w64((mx - st.m) * x.c > RESCALE_LOG2)) {
+        const float m_new = fmaxf(st.m, mx);
+        const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * x.c);
+        st.m = m_new;
+        st.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
+    }
+    const float mc = st.m * x.c;
+
+    // P = 2^(S c - m c) in bf16, packed in MFMA B-operand order: k-step k of
+    // the PV product takes keys 16k + 4hw + {0..3} and 16k + 8 + 4hw + {0..3},
+    // i.e. accumulator rows i = 2(k%2) and 2(k%2)+1 of block k/2.  The row
+    // sum adds exactly these bf16 weights (v_dot2 with ones).
+    bf16x8 pf[PS];
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < PS; ++k) {
+        const int kb = k >> 1, i0 = 2 * (k & 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pf[k][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][i0 * 4 + j], x.c, -mc));
+            pf[k][4 + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][(i0 + 1) * 4 + j], x.c, -mc));
+        }
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int j = 0; j < 8; j += 4) {
+            rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][j], pf[k][j + 1]}, one, rs0, false);
+            rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][j + 2], pf[k][j + 3]}, one, rs1, false);
+        }
+    }
+    st.l += rs0 + rs1;
+
+    // O^T += V^T P^T.  V^T comes from the row-major V tile via the
+    // transposing read: 16 lanes read 4 key rows x 16 d, each lane ending up
+    // with 4 keys of one d column.
+#pragma unroll
+    for (int k = 0; k < PS; ++k) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const LDS_AS char *vp = vcur + lo.v_rd[db] + k * 16 * 2 * D;
+            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)vp);
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vp + 8 * 2 * D));
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[k], st.o[db], 0, 0, 0);
+        }
+    }
+}
+
 template <int D, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(2)))
 void fa_fwd_kernel(const FaArgs a) {
-    constexpr int NCH = D / 8;
-    constexpr int KS = D / 16;       // k-steps of S^T = K Q^T
-    constexpr int NDB = D / 32;      // 32-row blocks of O^T
-    constexpr int NKB = BN / 32;     // 32-key blocks of S^T
-    constexpr int PS = BN / 16;      // k-steps of O^T += V^T P^T
-    constexpr int TILE = BN * D * 2; // bytes of one K or V tile
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // [buf 0,1] x [K, V]
+    constexpr int KS = D / 16, NDB = D / 32, NCH = D / 8;
+    constexpr int TILE = BN * D * 2;   // bytes of one K or V tile
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K0 V0 K1 V1
+    LDS_AS char *const lds = (LDS_AS char *)smem;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -163,134 +295,82 @@ void fa_fwd_kernel(const FaArgs a) {
     const int split = rest % a.nsplit;
     const int bh = rest / a.nsplit;
     const int b = bh / a.H, hh = bh % a.H;
-
     const int kv_begin = split * a.split_len;
-    const int kv_end = min(a.kv_len, kv_begin + a.split_len);
-    const float c = a.scale_log2;
 
+    TileCtx x;
+    x.kv_end = min(a.kv_len, kv_begin + a.split_len);
+    x.c = a.scale_log2;
+    x.wave = wave;
+    x.hw = hw;
+    x.k_stride = (int)(a.k_ss * 2);
+    x.v_stride = (int)(a.v_ss * 2);
     const __bf16 *qb = a.q + b * a.q_sb + hh * a.q_sh;
-    const __bf16 *kb = a.k + b * a.k_sb + hh * a.k_sh;
-    const __bf16 *vb = a.v + b * a.v_sb + hh * a.v_sh;
+    x.kr = make_rsrc(a.k + b * a.k_sb + hh * a.k_sh, ((int64_t)(a.kv_len - 1) * a.k_ss + D) * 2);
+    x.vr = make_rsrc(a.v + b * a.v_sb + hh * a.v_sh, ((int64_t)(a.kv_len - 1) * a.v_ss + D) * 2);
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(qb, ((int64_t)(a.Sq - 1) * a.q_ss + D) * 2);
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kb, ((int64_t)(a.kv_len - 1) * a.k_ss + D) * 2);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vb, ((int64_t)(a.kv_len - 1) * a.v_ss + D) * 2);
 
-    // Start streaming the first K/V tile before touching Q.
-    load_tile<D, false>(kr, a.k_ss * 2, kv_begin, smem, wave, lane);
-    load_tile<D, true>(vr, a.v_ss * 2, kv_begin, smem + TILE, wave, lane);
+    LaneOffsets<D> lo;
+#pragma unroll
+    for (int n = 0; n < LaneOffsets<D>::PER_THREAD; ++n) {
+        const int idx = (n * NWAVES + wave) * 64 + lane;   // physical chunk index in the tile
+        const int r = idx / NCH, p = idx % NCH;
+        lo.k_src[n] = r * x.k_stride + swz_k<D>(r, p) * 16;   // the swizzle is an involution
+        lo.v_src[n] = r * x.v_stride + swz_v<D>(r, p) * 16;
+    }
+#pragma unroll
+    for (int k = 0; k < KS; ++k) lo.k_rd[k] = l32 * 2 * D + swz_k<D>(l32, 2 * k + hw) * 16;
+    {
+        const int li = lane & 15, g = (lane >> 4) & 1;
+        const int r0 = 4 * hw + (li >> 2);   // + 16k (+8) added as immediates
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int col = 32 * db + 16 * g + 4 * (li & 3);
+            lo.v_rd[db] = r0 * 2 * D + swz_v<D>(r0, col >> 3) * 16 + ((col >> 2) & 1) * 8;
+        }
+    }
+
+    const int ntiles = (x.kv_end - kv_begin + BN - 1) / BN;
+    dma_tile<D>(x.kr, lo.k_src, kv_begin * x.k_stride, lds, wave);
+    dma_tile<D>(x.vr, lo.v_src, kv_begin * x.v_stride, lds + TILE, wave);
 
     // Q^T as the B operand: lane holds 8 consecutive d of its query row per k-step.
     const int qrow = qt * BM + wave * 32 + l32;
     bf16x8 qf[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(qr, (int)((int64_t)qrow * a.q_ss * 2) + (2 * s + hw) * 16, 0, 0);
-        qf[s] = __builtin_bit_cast(bf16x8, w);
+    for (int k = 0; k < KS; ++k) {
+        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            qr, (int)((int64_t)qrow * a.q_ss * 2) + (2 * k + hw) * 16, 0, 0));
+        qf[k] = __builtin_bit_cast(bf16x8, w);
     }
 
-    f32x16 acc_o[NDB];
+    RowState<D> st;
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) acc_o[i] = f32x16{};
-    float m_run = -1e30f;   // running row max of the raw scores (finite start: no inf - inf)
-    float l_run = 0.f;      // this half-wave's share of the running row sum
+    for (int i = 0; i < NDB; ++i) st.o[i] = f32x16{};
+    st.m = -1e30f;   // finite start: no inf - inf
+    st.l = 0.f;
 
-    const int ntiles = (kv_end - kv_begin + BN - 1) / BN;
-    for (int t = 0; t < ntiles; ++t) {
+    // Two tiles per trip so that each tile's buffer is a compile-time offset.
+    // Before each barrier this wave waits for its own outstanding loads --
+    // at that point only the DMA of the tile about to be used (and, first
+    // time round, Q) -- so after the barrier the whole tile is in LDS and
+    // every wave is done with the other buffer, which the prefetch refills.
+    // The wait is explicit: the compiler's own accounting does not cover
+    // LDS written by DMA across the loop back-edge.
+    int t = 0;
+    for (; t + 2 <= ntiles; t += 2) {
         const int t0 = kv_begin + t * BN;
-        char *ktile = smem + (t & 1) * 2 * TILE;
-        char *vtile = ktile + TILE;
-        // Tile t has landed (own loads) and every wave is done with the other buffer.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (t + 1 < ntiles) {
-            char *nk = smem + ((t + 1) & 1) * 2 * TILE;
-            load_tile<D, false>(kr, a.k_ss * 2, t0 + BN, nk, wave, lane);
-            load_tile<D, true>(vr, a.v_ss * 2, t0 + BN, nk + TILE, wave, lane);
-        }
-
-        // S^T = K Q^T: acc_s[kb][i*4+j] is the score of key t0 + 32kb + 8i + 4hw + j
-        // against query qrow.
-        f32x16 acc_s[NKB];
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2) {
-            acc_s[kb2] = f32x16{};
-            const int r = 32 * kb2 + l32;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int p = swz_k<D>(r, 2 * s + hw);
-                const u32x4 w = *(const LDS_AS u32x4 *)((LDS_AS char *)ktile + r * (2 * D) + p * 16);
-                acc_s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), qf[s],
-                                                                     acc_s[kb2], 0, 0, 0);
-            }
-        }
-
-        // Keys at or past kv_end (ragged tail, audio padding) get -inf.
-        if (t0 + BN > kv_end) {
-#pragma unroll
-            for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = t0 + 32 * kb2 + 8 * (e >> 2) + 4 * hw + (e & 3);
-                    if (key >= kv_end) acc_s[kb2][e] = -INFINITY;
-                }
-        }
-
-        // Online softmax in the exp2 domain.
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc_s[kb2][e]);
-        mx = xhalf_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-        m_run = m_new;
-        const float mc = m_new * c;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb2 = 0; kb2 < NKB; ++kb2)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(fmaf(acc_s[kb2][e], c, -mc));
-                acc_s[kb2][e] = pe;
-                rs += pe;
-            }
-        l_run = l_run * alpha + rs;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc_o[db][e] *= alpha;
-
-        // O^T += V^T P^T.  k-step s covers keys 16s..16s+15 of the tile; this
-        // half-wave contributes keys 16s + 4hw + {0..3} and 16s + 8 + 4hw + {0..3}.
-#pragma unroll
-        for (int s = 0; s < PS; ++s) {
-            const int kb2 = s >> 1, i0 = 2 * (s & 1);
-            bf16x8 pf;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pf[j] = (__bf16)acc_s[kb2][i0 * 4 + j];
-                pf[4 + j] = (__bf16)acc_s[kb2][(i0 + 1) * 4 + j];
-            }
-            const int li = lane & 15, g = (lane >> 4) & 1;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const int col = 32 * db + 16 * g + 4 * (li & 3);
-                const int cch = col >> 3, half = (col >> 2) & 1;
-                const int r0 = 16 * s + 4 * hw + (li >> 2);
-                const int r1 = r0 + 8;
-                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (LDS_AS i16x4 *)((LDS_AS char *)vtile + r0 * (2 * D) + swz_v<D>(r0, cch) * 16 + half * 8));
-                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (LDS_AS i16x4 *)((LDS_AS char *)vtile + r1 * (2 * D) + swz_v<D>(r1, cch) * 16 + half * 8));
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-                acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc_o[db], 0, 0, 0);
-            }
-        }
+        tile_barrier();
+        attend_tile<D>(x, lo, qf, st, t0, true, lds, lds + TILE, lds + 2 * TILE, lds + 3 * TILE);
+        tile_barrier();
+        attend_tile<D>(x, lo, qf, st, t0 + BN, t + 2 < ntiles, lds + 2 * TILE, lds + 3 * TILE, lds, lds + TILE);
+    }
+    if (t < ntiles) {
+        tile_barrier();
+        attend_tile<D>(x, lo, qf, st, kv_begin + t * BN, false, lds, lds + TILE, lds + 2 * TILE, lds + 3 * TILE);
     }
 
-    // acc_o[db][i*4+j] is O^T[d = 32db + 8i + 4hw + j][query qrow] (unnormalised).
-    const float l_tot = xhalf_sum(l_run);
+    // st.o[db][i*4+j] is O^T[d = 32db + 8i + 4hw + j][query qrow] (unnormalised).
+    const float l_tot = xhalf_sum(st.l);
     if (!SPLIT) {
         if (qrow < a.Sq) {
             const float inv = 1.0f / l_tot;
@@ -301,7 +381,7 @@ void fa_fwd_kernel(const FaArgs a) {
                 for (int i = 0; i < 4; ++i) {
                     bf16x4 ov;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(acc_o[db][i * 4 + j] * inv);
+                    for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(st.o[db][i * 4 + j] * inv);
                     *(bf16x4 *)(orow + 32 * db + 8 * i + 4 * hw) = ov;
                 }
         }
@@ -314,11 +394,11 @@ void fa_fwd_kernel(const FaArgs a) {
             for (int i = 0; i < 4; ++i) {
                 f32x4 ov;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) ov[j] = acc_o[db][i * 4 + j];
+                for (int j = 0; j < 4; ++j) ov[j] = st.o[db][i * 4 + j];
                 *(f32x4 *)(po + 32 * db + 8 * i + 4 * hw) = ov;
             }
         if (hw == 0) {
-            a.part_ml[prow * 2 + 0] = m_run * c;
+            a.part_ml[prow * 2 + 0] = st.m * x.c;
             a.part_ml[prow * 2 + 1] = l_tot;
         }
     }
