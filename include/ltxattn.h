@@ -149,12 +149,16 @@ int ltxattn_last_hip_error(const ltxattn_handle *h);
 /* Per-kind timing with HIP events recorded on the call's stream.
  * ltxattn_profile_begin creates events for up to max_calls block calls
  * (created here, outside any timed region); each later block call records
- * one event before the first kind and one after each kind.
- * ltxattn_profile_read waits for the recorded events and writes, for each
- * recorded call c < *n_calls (at most max_calls), ms[c*5 + kind] = the time
- * of that kind (0 if skipped) and ms[c*5 + 4] = the whole call.
+ * events around every kind.  ltxattn_profile_read waits for the recorded
+ * events and writes LTXATTN_PROFILE_FLOATS floats per recorded call
+ * c < *n_calls (at most max_calls), in milliseconds:
+ *   ms[c*9 + kind]      that kind (0 if skipped);
+ *   ms[c*9 + 4]         the whole call;
+ *   ms[c*9 + 5 + kind]  that kind's attention kernels only (the same value
+ *                       as long as no kind runs preparation work).
  * ltxattn_profile_end stops recording and frees the events.
  * Errors: INVALID_ARG (null pointer, max_calls < 1), HIP. */
+#define LTXATTN_PROFILE_FLOATS 9
 int ltxattn_profile_begin(ltxattn_handle *h, int32_t max_calls);
 int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_t *n_calls);
 int ltxattn_profile_end(ltxattn_handle *h);

@@ -91,7 +91,8 @@ def test_full_size_sampled(lt, torch, cfg):
     got = run_block(lt, torch, w, inputs)
     rng = np.random.default_rng(100 + cfg)
     rows = {k: sample_rows(rng, w.batch, w.heads,
-                           w.video_len if k in ("video_self", "a2v") else w.audio_len)
+                           w.video_len if k in ("video_self", "a2v") else w.audio_len,
+                           n_random=96 if k == "video_self" else 24)
             for k in KINDS}
     want = oracle.block_attention_rows(inputs, w.audio_kv_len, rows)
     for k in KINDS:
@@ -107,6 +108,24 @@ def test_full_size_sampled(lt, torch, cfg):
         hi = bound[k].max(axis=1, keepdims=True) + 2e-2
         lo = bound[k].min(axis=1, keepdims=True) - 2e-2
         assert np.all(o <= hi) and np.all(o >= lo), f"cfg{cfg} {k}: output outside hull of valid V"
+
+
+def test_tail_round_split(lt, torch):
+    """8 heads x 9216 video queries = 576 work items of 128 queries.  On a
+    256-CU MI355X each XCD's group holds one head's 72 items; with 2 resident
+    workgroups per CU the last 8 query tiles of each head run as key-range
+    parts merged by the combine kernel.  Rows there and elsewhere must match."""
+    w = synth.Workload(31, "tail split", 1, 8, 128, 9216, 64, 64)
+    inputs = synth.make_block_inputs(w)
+    got = run_block(lt, torch, w, inputs, kinds=("video_self",))
+    rng = np.random.default_rng(31)
+    rows = []
+    for h in range(w.heads):
+        for i in list(rng.integers(8192, 9216, 6)) + [8192, 9215, int(rng.integers(0, 8192))]:
+            rows.append((0, h, int(i)))
+    rows = np.array(rows, np.int64)
+    want = oracle.block_attention_rows(inputs, w.audio_kv_len, {"video_self": rows})["video_self"]
+    compare(got["video_self"][rows[:, 0], rows[:, 2], rows[:, 1], :], want, "tail-split rows")
 
 
 def needle_inputs(B, H, D, Sv, La, Lk, video_pos, audio_pos, seed=7):

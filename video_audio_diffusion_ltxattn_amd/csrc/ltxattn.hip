@@ -9,9 +9,10 @@
 // accumulation and fp32 softmax statistics.
 //
 // Kernel design (gfx950, 64-wide waves):
-//  * A workgroup is 4 waves; each wave owns 32 query rows, so a workgroup
-//    covers BM = 128 query rows of one (batch, head).  Keys stream through
-//    in tiles of BN = 64.
+//  * Each wave owns 32 query rows; a workgroup of NW = 8 waves (video
+//    self-attention) or 4 waves (the rest) covers BM = 32 * NW query rows of
+//    one (batch, head), and every K/V tile it loads serves all of them.
+//    Keys stream through in tiles of BN = 64.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K is the A operand (from LDS) and Q^T the B
 //    operand (held in registers for the whole kernel).  In the 32x32
@@ -26,22 +27,28 @@
 //    permuted freely, the key order the score accumulator happens to give
 //    each half-wave is simply used for V as well.
 //  * K and V tiles go HBM -> LDS with buffer_load ... lds (no VGPR
-//    staging), double-buffered: the next tile streams in while the current
-//    one is consumed.  Buffer range checks return zeros for rows past the
-//    valid length, which handles ragged tails and the audio key padding
-//    without branches; the padded keys are never read.
+//    staging), double-buffered.  K runs one tile ahead of V: while the
+//    softmax of tile t runs on the VALU, the MFMAs compute the scores of
+//    tile t+1.  Buffer range checks return zeros for rows past the valid
+//    length, which handles ragged tails and the audio key padding without
+//    branches; the padded keys are never read.
 //  * LDS rows are XOR-swizzled per tensor so the K reads (ds_read_b128, 16
 //    rows per pass) and the transposed V reads (4 rows per pass) are free
 //    of bank conflicts.
 //  * Workgroups are remapped so that each of the 8 XCDs works through a
 //    contiguous range of (batch, head) slices and the K/V of a head stay
 //    in that XCD's L2.
-//  * v2a has only La = 126..256 queries per head but 15360..27280 keys: it
-//    splits the key range over workgroups, each writing an unnormalised
-//    fp32 partial O plus its row max and row sum, and a combine kernel
-//    merges the partials by log-sum-exp in a fixed order (the same softmax
-//    statistics merge that the context-parallel v2a of TensorRT-Model-
-//    Connect PR #1586 does across ranks).
+//  * A work item is one (batch, head, 128-query tile).  Items can be split
+//    over the key range: each part writes an unnormalised fp32 partial O
+//    plus its row max and row sum, and a combine kernel merges the parts by
+//    log-sum-exp in a fixed order (the same softmax statistics merge that
+//    the context-parallel v2a of TensorRT-Model-Connect PR #1586 does
+//    across ranks).  v2a (126..256 audio queries per head against
+//    15360..27280 video keys) splits every item so the latency-bound audio
+//    side fills the chip.  Video self-attention splits only the items of an
+//    incomplete last round of workgroups: with 2 resident workgroups per CU,
+//    3840 items would leave the 8th round half empty, so the last 256 items
+//    run as 512 half-length parts instead.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -63,12 +70,12 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BM = 128;          // query rows per workgroup
 constexpr int BN = 64;           // keys per tile
-constexpr int NWAVES = 4;
-constexpr int NTHREADS = 64 * NWAVES;
-constexpr int NSPLIT_MAX = 16;   // key-range splits of the v2a pass
+constexpr int BM_MAX = 256;      // most query rows per workgroup (8 waves x 32)
+constexpr int WAVES_PER_CU = 8;  // 2 per SIMD: the register budget of the attention kernel
+constexpr int NSPLIT_MAX = 16;   // key-range parts of a split work item
 constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int PROF_EVENTS = 5;          // events per profiled block call
 
 struct FaArgs {
     const __bf16 *q, *k, *v;
@@ -77,10 +84,15 @@ struct FaArgs {
     int64_t v_sb, v_ss, v_sh;
     __bf16 *o;
     int64_t o_sb, o_ss, o_sh;
-    float *part_o;    // split pass: [bh][split][q_pad][D] fp32, unnormalised
-    float *part_ml;   // split pass: [bh][split][q_pad][2] = (row max * log2e/sqrt(D), row sum)
+    float *part_o;    // split items: [split index][part][bm][D] fp32, unnormalised
+    float *part_ml;   // split items: [split index][part][bm][2] = (row max * log2e/sqrt(D), row sum)
     int B, H, Sq, kv_len;
-    int n_qtiles, nsplit, split_len, q_pad;
+    int n_qtiles;     // query tiles per (batch, head); item = bh * n_qtiles + qtile
+    // Work is dealt in G groups (G = 8, one per XCD, or 1).  Group g owns items
+    // [g * ipg, (g + 1) * ipg): the first wpg run whole, one workgroup each;
+    // the remaining ipg - wpg run as nsplit parts of split_len keys.
+    int groups, ipg, wpg;
+    int nsplit, split_len;
     float scale_log2;  // log2(e) / sqrt(D)
     int total;         // workgroups in the grid
 };
@@ -89,7 +101,7 @@ struct CombineArgs {
     const float *part_o, *part_ml;
     __bf16 *o;
     int64_t o_sb, o_ss, o_sh;
-    int B, H, Sq, nsplit, q_pad;
+    int H, Sq, bm, n_qtiles, ipg, wpg, n_split_items, nsplit;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
@@ -111,10 +123,10 @@ template <int D> __device__ __forceinline__ int swz_v(int r, int c) {
 }
 
 // Per-lane byte offsets that do not change from tile to tile.
-template <int D>
+template <int D, int NW>
 struct LaneOffsets {
     static constexpr int KS = D / 16, NDB = D / 32;
-    static constexpr int PER_THREAD = BN * (D / 8) / NTHREADS;   // DMA chunks per thread per tile
+    static constexpr int PER_THREAD = BN * (D / 8) / (64 * NW);   // DMA chunks per thread per tile
     int k_rd[KS];          // K tile, ds_read_b128 for k-step s (key block 0; block 1 is +32 rows)
     int v_rd[NDB];         // V tile, ds_read_b64_tr_b16 for d block db (k-step s adds 16s rows)
     int k_src[PER_THREAD]; // global byte offset (minus the tile's first row) of each K chunk
@@ -126,12 +138,12 @@ struct LaneOffsets {
 // fills 1 KB of LDS contiguously (lane i -> +16*i); the swizzle is applied by
 // choosing which global chunk each lane fetches (src).  Rows past the
 // resource's range read as zeros.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rsrc, const int *src, int soff,
                                          LDS_AS char *tile, int wave) {
 #pragma unroll
-    for (int n = 0; n < LaneOffsets<D>::PER_THREAD; ++n)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(tile + (n * NWAVES + wave) * 1024), 16,
+    for (int n = 0; n < LaneOffsets<D, NW>::PER_THREAD; ++n)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void *)(tile + (n * NW + wave) * 1024), 16,
                                                  src[n], soff, 0, 0);
 }
 
@@ -172,36 +184,29 @@ struct TileCtx {
     int wave, hw;
 };
 
-// One key tile: prefetch the next tile into the other buffer, then
-// S^T = K Q^T, online softmax, O^T += V^T P^T.  The LDS tiles are passed as
-// restrict pointers: the compiler can then tell that the reads of this tile
-// do not touch the buffer the prefetch is writing, and does not wait for it.
-template <int D>
-__device__ __forceinline__ void attend_tile(const TileCtx &x, const LaneOffsets<D> &lo, const bf16x8 *qf,
-                                            RowState<D> &st, int t0, bool prefetch,
-                                            const LDS_AS char *__restrict__ kcur,
-                                            const LDS_AS char *__restrict__ vcur,
-                                            LDS_AS char *__restrict__ knext,
-                                            LDS_AS char *__restrict__ vnext) {
-    constexpr int KS = D / 16, NDB = D / 32, NKB = BN / 32, PS = BN / 16;
-    if (prefetch) {
-        dma_tile<D>(x.kr, lo.k_src, (t0 + BN) * x.k_stride, knext, x.wave);
-        dma_tile<D>(x.vr, lo.v_src, (t0 + BN) * x.v_stride, vnext, x.wave);
-    }
-
-    // S^T = K Q^T: s[kb][i*4+j] = score of key t0 + 32kb + 8i + 4hw + j against this lane's query.
-    f32x16 s[NKB];
+// S^T = K Q^T for one tile: s[kb][i*4+j] is the score of key t0 + 32kb + 8i +
+// 4hw + j against this lane's query.
+template <int D, int NW>
+__device__ __forceinline__ void scores(const LaneOffsets<D, NW> &lo, const bf16x8 *qf,
+                                       const LDS_AS char *__restrict__ ktile, f32x16 *s) {
+    constexpr int KS = D / 16, NKB = BN / 32;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    // k outer, key block inner: the NKB accumulator chains are independent,
+    // so consecutive MFMAs do not wait on each other's results.
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-            const u32x4 w = *(const LDS_AS u32x4 *)(kcur + kb * 32 * 2 * D + lo.k_rd[k]);
+    for (int k = 0; k < KS; ++k) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const u32x4 w = *(const LDS_AS u32x4 *)(ktile + kb * 32 * 2 * D + lo.k_rd[k]);
             s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), qf[k], s[kb], 0, 0, 0);
         }
     }
+}
 
-    // Keys at or past kv_end (ragged tail, audio padding) get -inf.
+// Keys at or past kv_end (ragged tail, audio padding) get -inf.
+__device__ __forceinline__ void mask_tail(const TileCtx &x, int t0, f32x16 *s) {
+    constexpr int NKB = BN / 32;
     if (t0 + BN > x.kv_end) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -211,8 +216,14 @@ __device__ __forceinline__ void attend_tile(const TileCtx &x, const LaneOffsets<
                 if (key >= x.kv_end) s[kb][e] = -INFINITY;
             }
     }
+}
 
-    // Row max: two independent chains, then the other half-wave.
+// Online softmax, first half: the tile's row max, and a lazy update of the
+// max in use -- O and the row sum are rescaled only if some row's max grew
+// by more than 2^RESCALE_LOG2.
+template <int D>
+__device__ __forceinline__ void update_max(const TileCtx &x, const f32x16 *s, RowState<D> &st) {
+    constexpr int NDB = D / 32, NKB = BN / 32;
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -232,14 +243,19 @@ __device__ __forceinline__ void attend_tile(const TileCtx &x, const LaneOffsets<
 #pragma unroll
             for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
     }
-    const float mc = st.m * x.c;
+}
 
-    // P = 2^(S c - m c) in bf16, packed in MFMA B-operand order: k-step k of
-    // the PV product takes keys 16k + 4hw + {0..3} and 16k + 8 + 4hw + {0..3},
-    // i.e. accumulator rows i = 2(k%2) and 2(k%2)+1 of block k/2.  The row
-    // sum adds exactly these bf16 weights (v_dot2 with ones).
-    bf16x8 pf[PS];
+// Online softmax, second half: P = 2^(S c - m c) in bf16, packed in MFMA
+// B-operand order -- k-step k of the PV product takes keys 16k + 4hw +
+// {0..3} and 16k + 8 + 4hw + {0..3}, i.e. accumulator rows i = 2(k%2) and
+// 2(k%2)+1 of block k/2 -- and the row sum of exactly these bf16 weights
+// (v_dot2 with ones).
+template <int D>
+__device__ __forceinline__ void probs(const TileCtx &x, const f32x16 *s, RowState<D> &st, bf16x8 *pf) {
+    constexpr int PS = BN / 16;
+    const float mc = st.m * x.c;
     float rs0 = 0.f, rs1 = 0.f;
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int k = 0; k < PS; ++k) {
         const int kb = k >> 1, i0 = 2 * (k & 1);
@@ -248,7 +264,6 @@ __device__ __forceinline__ void attend_tile(const TileCtx &x, const LaneOffsets<
             pf[k][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][i0 * 4 + j], x.c, -mc));
             pf[k][4 + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][(i0 + 1) * 4 + j], x.c, -mc));
         }
-        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
         for (int j = 0; j < 8; j += 4) {
             rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][j], pf[k][j + 1]}, one, rs0, false);
@@ -256,15 +271,20 @@ __device__ __forceinline__ void attend_tile(const TileCtx &x, const LaneOffsets<
         }
     }
     st.l += rs0 + rs1;
+}
 
-    // O^T += V^T P^T.  V^T comes from the row-major V tile via the
-    // transposing read: 16 lanes read 4 key rows x 16 d, each lane ending up
-    // with 4 keys of one d column.
+// O^T += V^T P^T for one tile.  V^T comes from the row-major V tile via the
+// transposing read: 16 lanes read 4 key rows x 16 d, each lane ending up
+// with 4 keys of one d column.
+template <int D, int NW>
+__device__ __forceinline__ void accumulate_pv(const LaneOffsets<D, NW> &lo, const LDS_AS char *__restrict__ vtile,
+                                              const bf16x8 *pf, RowState<D> &st) {
+    constexpr int NDB = D / 32, PS = BN / 16;
 #pragma unroll
     for (int k = 0; k < PS; ++k) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const LDS_AS char *vp = vcur + lo.v_rd[db] + k * 16 * 2 * D;
+            const LDS_AS char *vp = vtile + lo.v_rd[db] + k * 16 * 2 * D;
             const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)vp);
             const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vp + 8 * 2 * D));
             const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -273,32 +293,67 @@ __device__ __forceinline__ void attend_tile(const TileCtx &x, const LaneOffsets<
     }
 }
 
-template <int D, bool SPLIT>
-__global__ __attribute__((amdgpu_flat_work_group_size(NTHREADS, NTHREADS), amdgpu_waves_per_eu(2)))
+// One pipelined step, for tile t whose scores s_cur are already computed.
+// K runs one tile ahead of V: this step prefetches K of tile t+2 and V of
+// tile t+1, settles the max of tile t, then -- in one straight-line block
+// the scheduler can interleave -- computes the scores of tile t+1 (MFMA)
+// while the probabilities of tile t are formed (VALU), and accumulates
+// P V of tile t.  The scores of t+1 are computed even past the last tile
+// (from a stale buffer, in bounds) and then simply not used.  Each tensor
+// has two LDS buffers; the tiles are restrict pointers, so the compiler
+// knows the reads do not touch the buffers being refilled.
+template <int D, int NW>
+__device__ __forceinline__ void pipeline_step(const TileCtx &x, const LaneOffsets<D, NW> &lo, const bf16x8 *qf,
+                                              RowState<D> &st, const f32x16 *s_cur, f32x16 *s_next,
+                                              int t0, int ntiles_left,
+                                              const LDS_AS char *__restrict__ k_next,   // K of t+1
+                                              const LDS_AS char *__restrict__ v_cur,    // V of t
+                                              LDS_AS char *__restrict__ k_fill,         // <- K of t+2
+                                              LDS_AS char *__restrict__ v_fill) {       // <- V of t+1
+    constexpr int PS = BN / 16;
+    if (ntiles_left > 2) dma_tile<D, NW>(x.kr, lo.k_src, (t0 + 2 * BN) * x.k_stride, k_fill, x.wave);
+    if (ntiles_left > 1) dma_tile<D, NW>(x.vr, lo.v_src, (t0 + BN) * x.v_stride, v_fill, x.wave);
+    update_max<D>(x, s_cur, st);
+    bf16x8 pf[PS];
+    scores<D, NW>(lo, qf, k_next, s_next);
+    probs<D>(x, s_cur, st, pf);
+    accumulate_pv<D, NW>(lo, v_cur, pf, st);
+    mask_tail(x, t0 + BN, s_next);
+}
+
+template <int D, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2)))
 void fa_fwd_kernel(const FaArgs a) {
-    constexpr int KS = D / 16, NDB = D / 32, NCH = D / 8;
+    constexpr int BM = 32 * NW;        // query rows per workgroup
+    constexpr int KS = D / 16, NDB = D / 32, NCH = D / 8, NKB = BN / 32;
     constexpr int TILE = BN * D * 2;   // bytes of one K or V tile
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K0 V0 K1 V1
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K0 K1 V0 V1
     LDS_AS char *const lds = (LDS_AS char *)smem;
+    LDS_AS char *const K0 = lds, *const K1 = lds + TILE, *const V0 = lds + 2 * TILE, *const V1 = lds + 3 * TILE;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hw = lane >> 5, l32 = lane & 31;
 
-    // Work item: query tile fastest, then key split, then (batch, head).
-    // Blocks are dealt to the 8 XCDs round-robin; remap so each XCD owns a
-    // contiguous range of work items (same heads -> shared K/V in its L2).
+    // Blocks are dealt to the 8 XCDs round-robin, so with 8 groups block
+    // bid runs on XCD bid % 8 and group g = bid % 8 keeps one contiguous
+    // range of items (same heads -> shared K/V) in that XCD's L2.  Within a
+    // group: whole items first (query tile fastest), then the parts of the
+    // split items.
     const int bid = blockIdx.x;
-    const int wid = (a.total % 8 == 0) ? (bid % 8) * (a.total / 8) + bid / 8 : bid;
-    const int qt = wid % a.n_qtiles;
-    const int rest = wid / a.n_qtiles;
-    const int split = rest % a.nsplit;
-    const int bh = rest / a.nsplit;
+    const int g = bid % a.groups, local = bid / a.groups;
+    const bool split_item = local >= a.wpg;
+    const int w = local - a.wpg;
+    const int part = split_item ? w % a.nsplit : 0;
+    const int item = g * a.ipg + (split_item ? a.wpg + w / a.nsplit : local);
+    const int split_idx = g * (a.ipg - a.wpg) + (split_item ? w / a.nsplit : 0);
+    const int qt = item % a.n_qtiles;
+    const int bh = item / a.n_qtiles;
     const int b = bh / a.H, hh = bh % a.H;
-    const int kv_begin = split * a.split_len;
+    const int kv_begin = part * a.split_len;
 
     TileCtx x;
-    x.kv_end = min(a.kv_len, kv_begin + a.split_len);
+    x.kv_end = split_item ? min(a.kv_len, kv_begin + a.split_len) : a.kv_len;
     x.c = a.scale_log2;
     x.wave = wave;
     x.hw = hw;
@@ -309,10 +364,10 @@ void fa_fwd_kernel(const FaArgs a) {
     x.vr = make_rsrc(a.v + b * a.v_sb + hh * a.v_sh, ((int64_t)(a.kv_len - 1) * a.v_ss + D) * 2);
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(qb, ((int64_t)(a.Sq - 1) * a.q_ss + D) * 2);
 
-    LaneOffsets<D> lo;
+    LaneOffsets<D, NW> lo;
 #pragma unroll
-    for (int n = 0; n < LaneOffsets<D>::PER_THREAD; ++n) {
-        const int idx = (n * NWAVES + wave) * 64 + lane;   // physical chunk index in the tile
+    for (int n = 0; n < LaneOffsets<D, NW>::PER_THREAD; ++n) {
+        const int idx = (n * NW + wave) * 64 + lane;   // physical chunk index in the tile
         const int r = idx / NCH, p = idx % NCH;
         lo.k_src[n] = r * x.k_stride + swz_k<D>(r, p) * 16;   // the swizzle is an involution
         lo.v_src[n] = r * x.v_stride + swz_v<D>(r, p) * 16;
@@ -330,8 +385,9 @@ void fa_fwd_kernel(const FaArgs a) {
     }
 
     const int ntiles = (x.kv_end - kv_begin + BN - 1) / BN;
-    dma_tile<D>(x.kr, lo.k_src, kv_begin * x.k_stride, lds, wave);
-    dma_tile<D>(x.vr, lo.v_src, kv_begin * x.v_stride, lds + TILE, wave);
+    dma_tile<D, NW>(x.kr, lo.k_src, kv_begin * x.k_stride, K0, wave);
+    dma_tile<D, NW>(x.vr, lo.v_src, kv_begin * x.v_stride, V0, wave);
+    if (ntiles > 1) dma_tile<D, NW>(x.kr, lo.k_src, (kv_begin + BN) * x.k_stride, K1, wave);
 
     // Q^T as the B operand: lane holds 8 consecutive d of its query row per k-step.
     const int qrow = qt * BM + wave * 32 + l32;
@@ -349,29 +405,33 @@ void fa_fwd_kernel(const FaArgs a) {
     st.m = -1e30f;   // finite start: no inf - inf
     st.l = 0.f;
 
-    // Two tiles per trip so that each tile's buffer is a compile-time offset.
     // Before each barrier this wave waits for its own outstanding loads --
-    // at that point only the DMA of the tile about to be used (and, first
-    // time round, Q) -- so after the barrier the whole tile is in LDS and
-    // every wave is done with the other buffer, which the prefetch refills.
-    // The wait is explicit: the compiler's own accounting does not cover
-    // LDS written by DMA across the loop back-edge.
+    // the DMA issued one step earlier (and, first time round, Q) -- so after
+    // the barrier those tiles are in LDS and every wave is done with the
+    // buffers the next prefetch refills.  The wait is explicit: the
+    // compiler's own accounting does not cover LDS written by DMA across the
+    // loop back-edge.  Two steps per trip keep every buffer a compile-time
+    // offset.
+    f32x16 sA[NKB], sB[NKB];
+    tile_barrier();
+    scores<D, NW>(lo, qf, K0, sA);
+    mask_tail(x, kv_begin, sA);
     int t = 0;
     for (; t + 2 <= ntiles; t += 2) {
         const int t0 = kv_begin + t * BN;
         tile_barrier();
-        attend_tile<D>(x, lo, qf, st, t0, true, lds, lds + TILE, lds + 2 * TILE, lds + 3 * TILE);
+        pipeline_step<D, NW>(x, lo, qf, st, sA, sB, t0, ntiles - t, K1, V0, K0, V1);
         tile_barrier();
-        attend_tile<D>(x, lo, qf, st, t0 + BN, t + 2 < ntiles, lds + 2 * TILE, lds + 3 * TILE, lds, lds + TILE);
+        pipeline_step<D, NW>(x, lo, qf, st, sB, sA, t0 + BN, ntiles - t - 1, K0, V1, K1, V0);
     }
     if (t < ntiles) {
         tile_barrier();
-        attend_tile<D>(x, lo, qf, st, kv_begin + t * BN, false, lds, lds + TILE, lds + 2 * TILE, lds + 3 * TILE);
+        pipeline_step<D, NW>(x, lo, qf, st, sA, sB, kv_begin + t * BN, ntiles - t, K1, V0, K0, V1);
     }
 
     // st.o[db][i*4+j] is O^T[d = 32db + 8i + 4hw + j][query qrow] (unnormalised).
     const float l_tot = xhalf_sum(st.l);
-    if (!SPLIT) {
+    if (!split_item) {
         if (qrow < a.Sq) {
             const float inv = 1.0f / l_tot;
             __bf16 *orow = a.o + b * a.o_sb + (int64_t)qrow * a.o_ss + hh * a.o_sh;
@@ -386,7 +446,7 @@ void fa_fwd_kernel(const FaArgs a) {
                 }
         }
     } else {
-        const int64_t prow = ((int64_t)bh * a.nsplit + split) * a.q_pad + qrow;
+        const int64_t prow = ((int64_t)split_idx * a.nsplit + part) * BM + (qrow - qt * BM);
         float *po = a.part_o + prow * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -404,26 +464,31 @@ void fa_fwd_kernel(const FaArgs a) {
     }
 }
 
-// Merge the split partials of one output row: M = max_r m_r,
-// L = sum_r l_r 2^(m_r - M), O = sum_r 2^(m_r - M) O_r / L, in split order.
+// Merge the parts of one output row of a split item: M = max_r m_r,
+// L = sum_r l_r 2^(m_r - M), O = sum_r 2^(m_r - M) O_r / L, in part order.
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void fa_combine_kernel(const CombineArgs a) {
     constexpr int TPR = D / 4;   // threads per output row, 4 floats each
     const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = gt / TPR;
+    const int BM = a.bm;
+    const int64_t row = gt / TPR;           // row of the split items' [item][bm] rows
     const int d4 = (int)(gt % TPR);
-    if (row >= (int64_t)a.B * a.H * a.Sq) return;
-    const int q = (int)(row % a.Sq);
-    const int bh = (int)(row / a.Sq);
+    if (row >= (int64_t)a.n_split_items * BM) return;
+    const int local = (int)(row / BM), r = (int)(row % BM);   // split index, row in tile
+    const int spg = a.ipg - a.wpg;
+    const int item = (local / spg) * a.ipg + a.wpg + local % spg;
+    const int qt = item % a.n_qtiles, bh = item / a.n_qtiles;
+    const int q = qt * BM + r;
+    if (q >= a.Sq) return;
     const int b = bh / a.H, hh = bh % a.H;
-    const int64_t base = (int64_t)bh * a.nsplit * a.q_pad + q;
+    const int64_t base = (int64_t)local * a.nsplit * BM + r;
     float M = -INFINITY;
-    for (int r = 0; r < a.nsplit; ++r) M = fmaxf(M, a.part_ml[(base + (int64_t)r * a.q_pad) * 2]);
+    for (int p = 0; p < a.nsplit; ++p) M = fmaxf(M, a.part_ml[(base + (int64_t)p * BM) * 2]);
     float L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < a.nsplit; ++r) {
-        const int64_t pr = base + (int64_t)r * a.q_pad;
+    for (int p = 0; p < a.nsplit; ++p) {
+        const int64_t pr = base + (int64_t)p * BM;
         const float w = __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - M);
         L += w * a.part_ml[pr * 2 + 1];
         const f32x4 ov = *(const f32x4 *)(a.part_o + pr * D + d4 * 4);
@@ -450,7 +515,7 @@ int check_tensor(const ltxattn_tensor &t, int B, int S, int H, int D, Extent *ex
     // One (batch, head) slice, plus the rows a kernel may touch past the end
     // of it (a query tile and a key tile), must be addressable with 32-bit
     // byte offsets, so that buffer range checks see every such row.
-    const int64_t slice = ((int64_t)(S + BM + BN) * t.stride_s + D) * 2;
+    const int64_t slice = ((int64_t)(S + BM_MAX + BN) * t.stride_s + D) * 2;
     if (slice >= ((int64_t)1 << 31) - 64) return LTXATTN_ERR_UNSUPPORTED;
     const int64_t span = (int64_t)(B - 1) * t.stride_b + (int64_t)(S - 1) * t.stride_s +
                          (int64_t)(H - 1) * t.stride_h + D;
@@ -504,10 +569,12 @@ int hip_fail(ltxattn_handle *h, hipError_t e) {
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// How many key-range splits the v2a pass uses: enough workgroups to give
-// every CU two, at least four key tiles per split, at most NSPLIT_MAX.
-int choose_nsplit(int base_wgs, int kv_len, int num_cus) {
-    int ns = ceil_div(2 * num_cus, base_wgs);
+// How many parts the v2a items are split into: enough workgroups to give
+// every CU two, at least four key tiles per part, at most NSPLIT_MAX.
+constexpr int LONG_ROWS = 1024;   // query and key rows from which 8-wave workgroups are used
+
+int choose_nsplit(int items, int kv_len, int num_cus) {
+    int ns = ceil_div(2 * num_cus, items);
     ns = ns < NSPLIT_MAX ? ns : NSPLIT_MAX;
     const int by_len = kv_len / (4 * BN);
     ns = ns < by_len ? ns : by_len;
@@ -515,8 +582,13 @@ int choose_nsplit(int base_wgs, int kv_len, int num_cus) {
 }
 
 int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len,
-                  bool allow_split, hipStream_t st) {
+                  bool split_all, hipStream_t st) {
     const int D = h->head_dim, H = h->heads;
+    // Long query and key streams (video self-attention) take 256-query
+    // workgroups: each K/V tile is then fetched once per 256 queries.  The
+    // others take 128 (more workgroups for the short, memory-bound ones).
+    const int NW = (Sq >= LONG_ROWS && kv_len >= LONG_ROWS && D == 128) ? 8 : 4;
+    const int BM = 32 * NW;
     FaArgs a;
     a.q = (const __bf16 *)io.q.data;
     a.k = (const __bf16 *)io.k.data;
@@ -528,34 +600,53 @@ int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, i
     a.o_sb = io.o.stride_b; a.o_ss = io.o.stride_s; a.o_sh = io.o.stride_h;
     a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
     a.n_qtiles = ceil_div(Sq, BM);
-    a.q_pad = a.n_qtiles * BM;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    const int base = B * H * a.n_qtiles;
-    int ns = allow_split ? choose_nsplit(base, kv_len, h->num_cus) : 1;
+    const int items = B * H * a.n_qtiles;
+    // One group per XCD when the items divide evenly, else a single group.
+    const int groups = (items % 8 == 0 && h->num_cus % 8 == 0) ? 8 : 1;
+    const int ipg = items / groups;
+    const int slots = WAVES_PER_CU / NW * h->num_cus / groups;   // workgroups resident per group
+    int spg = 0, ns = 1;                                 // split items per group, parts each
+    if (split_all) {
+        ns = choose_nsplit(items, kv_len, h->num_cus);
+        if (ns > 1) spg = ipg;
+    } else if (ipg > slots) {
+        // Split the items of an incomplete last round so that it fills its XCD.
+        const int rem = ipg % slots;
+        if (rem > 0 && 2 * rem <= slots) {
+            ns = slots / rem;
+            ns = ns < NSPLIT_MAX ? ns : NSPLIT_MAX;
+            const int by_len = kv_len / (4 * BN);
+            ns = ns < by_len ? ns : by_len;
+            if (ns > 1) spg = rem;
+        }
+    }
+    if (spg == 0) ns = 1;
     a.split_len = ceil_div(ceil_div(kv_len, ns), BN) * BN;
-    ns = ceil_div(kv_len, a.split_len);
+    ns = ceil_div(kv_len, a.split_len);   // every part holds at least one key
+    if (ns == 1) spg = 0;
     a.nsplit = ns;
+    a.groups = groups;
+    a.ipg = ipg;
+    a.wpg = ipg - spg;
     a.part_o = h->ws_o;
     a.part_ml = h->ws_ml;
-    a.total = base * ns;
-    const bool split = ns > 1;
-    if (split && (int64_t)base * ns * BM > h->ws_rows) return LTXATTN_ERR_INVALID_ARG;  // cannot happen
+    a.total = groups * (a.wpg + spg * ns);
+    const int n_split_items = groups * spg;
+    if ((int64_t)n_split_items * ns * BM > h->ws_rows) return LTXATTN_ERR_INVALID_ARG;  // cannot happen
 
-    if (D == 128) {
-        if (split) hipLaunchKernelGGL((fa_fwd_kernel<128, true>), dim3(a.total), dim3(NTHREADS), 0, st, a);
-        else hipLaunchKernelGGL((fa_fwd_kernel<128, false>), dim3(a.total), dim3(NTHREADS), 0, st, a);
-    } else {
-        if (split) hipLaunchKernelGGL((fa_fwd_kernel<64, true>), dim3(a.total), dim3(NTHREADS), 0, st, a);
-        else hipLaunchKernelGGL((fa_fwd_kernel<64, false>), dim3(a.total), dim3(NTHREADS), 0, st, a);
-    }
+    if (D == 128 && NW == 8) hipLaunchKernelGGL((fa_fwd_kernel<128, 8>), dim3(a.total), dim3(512), 0, st, a);
+    else if (D == 128) hipLaunchKernelGGL((fa_fwd_kernel<128, 4>), dim3(a.total), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((fa_fwd_kernel<64, 4>), dim3(a.total), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(h, e);
-    if (split) {
+    if (n_split_items > 0) {
         CombineArgs c;
         c.part_o = h->ws_o; c.part_ml = h->ws_ml;
         c.o = a.o; c.o_sb = a.o_sb; c.o_ss = a.o_ss; c.o_sh = a.o_sh;
-        c.B = B; c.H = H; c.Sq = Sq; c.nsplit = ns; c.q_pad = a.q_pad;
-        const int64_t threads = (int64_t)B * H * Sq * (D / 4);
+        c.H = H; c.Sq = Sq; c.bm = BM; c.n_qtiles = a.n_qtiles; c.ipg = ipg; c.wpg = a.wpg;
+        c.n_split_items = n_split_items; c.nsplit = ns;
+        const int64_t threads = (int64_t)n_split_items * BM * (D / 4);
         const int grid = ceil_div(threads, 256);
         if (D == 128) hipLaunchKernelGGL((fa_combine_kernel<128>), dim3(grid), dim3(256), 0, st, c);
         else hipLaunchKernelGGL((fa_combine_kernel<64>), dim3(grid), dim3(256), 0, st, c);
@@ -641,9 +732,12 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
     if (g.err != hipSuccess) { g_create_hip_error = (int)g.err; free(h); return LTXATTN_ERR_HIP; }
     e = hipDeviceGetAttribute(&h->num_cus, hipDeviceAttributeMultiprocessorCount, h->device);
     if (e != hipSuccess) { g_create_hip_error = (int)e; free(h); return LTXATTN_ERR_HIP; }
-    // Workspace of the v2a split pass: every (batch, head, query tile) times the
-    // largest split count, rows padded to whole query tiles.
-    h->ws_rows = (int64_t)h->max_batch * h->heads * ceil_div(h->max_audio_len, BM) * BM * NSPLIT_MAX;
+    // Workspace of the split items, BM rows per part: v2a splits every audio
+    // query tile of every (batch, head) into at most NSPLIT_MAX parts; the
+    // tail split of the other kinds uses at most one round of workgroups.
+    const int64_t v2a_rows = (int64_t)h->max_batch * h->heads * ceil_div(h->max_audio_len, 128) * NSPLIT_MAX * 128;
+    const int64_t tail_rows = (int64_t)WAVES_PER_CU / 4 * h->num_cus * BM_MAX;
+    h->ws_rows = v2a_rows > tail_rows ? v2a_rows : tail_rows;
     e = hipMalloc((void **)&h->ws_o, (size_t)h->ws_rows * h->head_dim * sizeof(float));
     if (e != hipSuccess) { g_create_hip_error = (int)e; (void)hipGetLastError(); free(h); return LTXATTN_ERR_OOM; }
     e = hipMalloc((void **)&h->ws_ml, (size_t)h->ws_rows * 2 * sizeof(float));
@@ -692,11 +786,12 @@ int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void 
     if (g.err != hipSuccess) return hip_fail(h, g.err);
     hipStream_t st = (hipStream_t)hip_stream;
     hipEvent_t *ev = nullptr;
-    if (h->events && h->prof_n < h->prof_max) ev = h->events + (int64_t)h->prof_n++ * 5;
+    if (h->events && h->prof_n < h->prof_max) ev = h->events + (int64_t)h->prof_n++ * PROF_EVENTS;
     hipError_t e;
     if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail(h, e);
 
-    // Fixed order: video self, a2v, v2a, audio self.  Event slot k+1 closes kind order[k].
+    // Fixed order: video self, a2v, v2a, audio self.  Event n + 1 closes the
+    // n-th kind in that order.
     const int order[4] = {LTXATTN_VIDEO_SELF, LTXATTN_A2V, LTXATTN_V2A, LTXATTN_AUDIO_SELF};
     for (int n = 0; n < 4; ++n) {
         const int k = order[n];
@@ -715,9 +810,9 @@ int ltxattn_profile_begin(ltxattn_handle *h, int32_t max_calls) {
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return hip_fail(h, g.err);
     if (h->events) ltxattn_profile_end(h);
-    h->events = (hipEvent_t *)calloc((size_t)max_calls * 5, sizeof(hipEvent_t));
+    h->events = (hipEvent_t *)calloc((size_t)max_calls * PROF_EVENTS, sizeof(hipEvent_t));
     if (!h->events) return LTXATTN_ERR_OOM;
-    for (int64_t i = 0; i < (int64_t)max_calls * 5; ++i) {
+    for (int64_t i = 0; i < (int64_t)max_calls * PROF_EVENTS; ++i) {
         hipError_t e = hipEventCreate(&h->events[i]);
         if (e != hipSuccess) {
             for (int64_t j = 0; j < i; ++j) (void)hipEventDestroy(h->events[j]);
@@ -736,22 +831,21 @@ int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return hip_fail(h, g.err);
     const int n = h->prof_n < max_calls ? h->prof_n : max_calls;
-    // Slot n+1 of a call closes kind order[n] (video self, a2v, v2a, audio self).
     const int kind_of_slot[4] = {LTXATTN_VIDEO_SELF, LTXATTN_A2V, LTXATTN_V2A, LTXATTN_AUDIO_SELF};
     for (int c = 0; c < n; ++c) {
-        hipEvent_t *ev = h->events + (int64_t)c * 5;
-        hipError_t e = hipEventSynchronize(ev[4]);
+        hipEvent_t *ev = h->events + (int64_t)c * PROF_EVENTS;
+        hipError_t e = hipEventSynchronize(ev[PROF_EVENTS - 1]);
         if (e != hipSuccess) return hip_fail(h, e);
+        float *out = ms + (int64_t)c * LTXATTN_PROFILE_FLOATS;
         for (int s = 0; s < 4; ++s) {
             float t = 0.f;
-            e = hipEventElapsedTime(&t, ev[s], ev[s + 1]);
-            if (e != hipSuccess) return hip_fail(h, e);
-            ms[c * 5 + kind_of_slot[s]] = t;
+            if ((e = hipEventElapsedTime(&t, ev[s], ev[s + 1])) != hipSuccess) return hip_fail(h, e);
+            out[kind_of_slot[s]] = t;
+            out[5 + kind_of_slot[s]] = t;   // no per-kind preparation: the kind is its kernels
         }
         float tot = 0.f;
-        e = hipEventElapsedTime(&tot, ev[0], ev[4]);
-        if (e != hipSuccess) return hip_fail(h, e);
-        ms[c * 5 + 4] = tot;
+        if ((e = hipEventElapsedTime(&tot, ev[0], ev[PROF_EVENTS - 1])) != hipSuccess) return hip_fail(h, e);
+        out[4] = tot;
     }
     *n_calls = n;
     return LTXATTN_OK;
@@ -761,7 +855,7 @@ int ltxattn_profile_end(ltxattn_handle *h) {
     if (!h) return LTXATTN_ERR_INVALID_ARG;
     if (!h->events) return LTXATTN_OK;
     DeviceGuard g(h->device);
-    for (int64_t i = 0; i < (int64_t)h->prof_max * 5; ++i) (void)hipEventDestroy(h->events[i]);
+    for (int64_t i = 0; i < (int64_t)h->prof_max * PROF_EVENTS; ++i) (void)hipEventDestroy(h->events[i]);
     free(h->events);
     h->events = nullptr;
     h->prof_max = h->prof_n = 0;

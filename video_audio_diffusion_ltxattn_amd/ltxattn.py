@@ -34,6 +34,7 @@ LTXATTN_AUDIO_SELF = 1
 LTXATTN_A2V = 2
 LTXATTN_V2A = 3
 LTXATTN_NUM_KINDS = 4
+LTXATTN_PROFILE_FLOATS = 9
 KIND_NAMES = ("video_self", "audio_self", "a2v", "v2a")
 KIND_INDEX = {n: i for i, n in enumerate(KIND_NAMES)}
 
@@ -144,16 +145,19 @@ def ltxattn_profile_begin(h, max_calls: int) -> None:
 
 
 def ltxattn_profile_read(h, max_calls: int):
-    """List of per-call dicts {kind name: ms, 'total': ms}."""
-    buf = (ctypes.c_float * (5 * max_calls))()
+    """Per recorded call: {kind: ms incl. its V transpose, 'total': ms,
+    'kernel': {kind: ms of the attention kernels only}}."""
+    nf = LTXATTN_PROFILE_FLOATS
+    buf = (ctypes.c_float * (nf * max_calls))()
     n = ctypes.c_int32()
     rc = _lib.ltxattn_profile_read(h, buf, int(max_calls), ctypes.byref(n))
     if rc != LTXATTN_OK:
         raise LtxattnError(rc, "ltxattn_profile_read")
     out = []
     for c in range(n.value):
-        d = {KIND_NAMES[k]: buf[c * 5 + k] for k in range(4)}
-        d["total"] = buf[c * 5 + 4]
+        d = {KIND_NAMES[k]: buf[c * nf + k] for k in range(4)}
+        d["total"] = buf[c * nf + 4]
+        d["kernel"] = {KIND_NAMES[k]: buf[c * nf + 5 + k] for k in range(4)}
         out.append(d)
     return out
 
