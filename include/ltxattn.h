@@ -17,13 +17,14 @@
  * multiple of the sequence-parallel degree), so the caller passes the
  * number of valid audio keys; audio key rows at or beyond it get weight
  * exactly zero and are never read.  Padded audio query rows are computed
- * like any other row.  Q and K arrive already normalised and rotated (the
- * context-parallel DiT of TensorRT-Model-Connect PR #1586 gathers the
- * "normed and rotated" keys), so no norm or RoPE happens here.
+ * like any other row.  Q and K arrive already normalised and rotary-embedded
+ * (the context-parallel DiT of TensorRT-Model-Connect PR #1586 all-gathers
+ * keys after those steps), so no norm or RoPE happens here.
  *
  * Precision: bf16 inputs and outputs with fp32 accumulation and fp32
- * softmax statistics (the DiT of PR #1586 is bf16 strongly typed with fp32
- * islands).  Outputs are rounded to bf16 to nearest even.
+ * softmax statistics (the DiT of PR #1586 keeps the network in bf16 with
+ * fp32 for norms and similar steps).  Outputs are rounded to bf16 to nearest
+ * even.
  *
  * Layout: every tensor is [B, S, H, D] bf16 with D contiguous (stride 1)
  * and explicit batch/sequence/head strides in elements, so both the packed
@@ -149,13 +150,14 @@ int ltxattn_last_hip_error(const ltxattn_handle *h);
 /* Per-kind timing with HIP events recorded on the call's stream.
  * ltxattn_profile_begin creates events for up to max_calls block calls
  * (created here, outside any timed region); each later block call records
- * events around every kind.  ltxattn_profile_read waits for the recorded
- * events and writes LTXATTN_PROFILE_FLOATS floats per recorded call
- * c < *n_calls (at most max_calls), in milliseconds:
- *   ms[c*9 + kind]      that kind (0 if skipped);
+ * events around every kind and one after each kind's attention kernel.
+ * ltxattn_profile_read waits for the recorded events and writes
+ * LTXATTN_PROFILE_FLOATS floats per recorded call c < *n_calls (at most
+ * max_calls), in milliseconds:
+ *   ms[c*9 + kind]      that kind, all its kernels (0 if skipped);
  *   ms[c*9 + 4]         the whole call;
- *   ms[c*9 + 5 + kind]  that kind's attention kernels only (the same value
- *                       as long as no kind runs preparation work).
+ *   ms[c*9 + 5 + kind]  that kind's attention kernel alone, without the
+ *                       combine kernel that merges key-range parts.
  * ltxattn_profile_end stops recording and frees the events.
  * Errors: INVALID_ARG (null pointer, max_calls < 1), HIP. */
 #define LTXATTN_PROFILE_FLOATS 9

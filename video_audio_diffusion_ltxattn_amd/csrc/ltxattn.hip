@@ -75,7 +75,7 @@ constexpr int BM_MAX = 256;      // most query rows per workgroup (8 waves x 32)
 constexpr int WAVES_PER_CU = 8;  // 2 per SIMD: the register budget of the attention kernel
 constexpr int NSPLIT_MAX = 16;   // key-range parts of a split work item
 constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
-constexpr int PROF_EVENTS = 5;          // events per profiled block call
+constexpr int PROF_EVENTS = 9;          // events per profiled block call
 
 struct FaArgs {
     const __bf16 *q, *k, *v;
@@ -581,8 +581,10 @@ int choose_nsplit(int items, int kv_len, int num_cus) {
     return ns < 1 ? 1 : ns;
 }
 
+// Launches the attention kernel (and, if some items were split, the combine
+// kernel); when `after_main` is given it is recorded between the two.
 int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len,
-                  bool split_all, hipStream_t st) {
+                  bool split_all, hipStream_t st, hipEvent_t after_main) {
     const int D = h->head_dim, H = h->heads;
     // Long query and key streams (video self-attention) take 256-query
     // workgroups: each K/V tile is then fetched once per 256 queries.  The
@@ -640,6 +642,7 @@ int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, i
     else hipLaunchKernelGGL((fa_fwd_kernel<64, 4>), dim3(a.total), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(h, e);
+    if (after_main && (e = hipEventRecord(after_main, st)) != hipSuccess) return hip_fail(h, e);
     if (n_split_items > 0) {
         CombineArgs c;
         c.part_o = h->ws_o; c.part_ml = h->ws_ml;
@@ -790,17 +793,21 @@ int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void 
     hipError_t e;
     if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail(h, e);
 
-    // Fixed order: video self, a2v, v2a, audio self.  Event n + 1 closes the
-    // n-th kind in that order.
+    // Fixed order: video self, a2v, v2a, audio self.  For the n-th kind in
+    // that order, event 1 + 2n follows its attention kernel (before any
+    // combine kernel) and event 2 + 2n closes the kind.
     const int order[4] = {LTXATTN_VIDEO_SELF, LTXATTN_A2V, LTXATTN_V2A, LTXATTN_AUDIO_SELF};
     for (int n = 0; n < 4; ++n) {
         const int k = order[n];
         if (on[k]) {
             const int kv_len = (k == LTXATTN_AUDIO_SELF || k == LTXATTN_A2V) ? Lk : Sv;
-            const int rc = run_attention(h, io->attn[k], B, q_rows[k], kv_len, k == LTXATTN_V2A, st);
+            const int rc = run_attention(h, io->attn[k], B, q_rows[k], kv_len, k == LTXATTN_V2A, st,
+                                         ev ? ev[1 + 2 * n] : nullptr);
             if (rc) return rc;
+        } else if (ev && (e = hipEventRecord(ev[1 + 2 * n], st)) != hipSuccess) {
+            return hip_fail(h, e);
         }
-        if (ev && (e = hipEventRecord(ev[n + 1], st)) != hipSuccess) return hip_fail(h, e);
+        if (ev && (e = hipEventRecord(ev[2 + 2 * n], st)) != hipSuccess) return hip_fail(h, e);
     }
     return LTXATTN_OK;
 }
@@ -838,10 +845,11 @@ int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_
         if (e != hipSuccess) return hip_fail(h, e);
         float *out = ms + (int64_t)c * LTXATTN_PROFILE_FLOATS;
         for (int s = 0; s < 4; ++s) {
-            float t = 0.f;
-            if ((e = hipEventElapsedTime(&t, ev[s], ev[s + 1])) != hipSuccess) return hip_fail(h, e);
-            out[kind_of_slot[s]] = t;
-            out[5 + kind_of_slot[s]] = t;   // no per-kind preparation: the kind is its kernels
+            float tot = 0.f, ker = 0.f;
+            if ((e = hipEventElapsedTime(&tot, ev[2 * s], ev[2 * s + 2])) != hipSuccess) return hip_fail(h, e);
+            if ((e = hipEventElapsedTime(&ker, ev[2 * s], ev[2 * s + 1])) != hipSuccess) return hip_fail(h, e);
+            out[kind_of_slot[s]] = tot;
+            out[5 + kind_of_slot[s]] = ker;
         }
         float tot = 0.f;
         if ((e = hipEventElapsedTime(&tot, ev[0], ev[PROF_EVENTS - 1])) != hipSuccess) return hip_fail(h, e);
