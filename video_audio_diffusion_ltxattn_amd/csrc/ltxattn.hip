@@ -56,6 +56,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "ltxattn.h"
 
 namespace {
@@ -464,6 +466,191 @@ void fa_fwd_kernel(const FaArgs a) {
     }
 }
 
+
+// ------------------------------------------------ resident short key streams
+// a2v and audio self-attention have at most a few hundred (audio) keys: a
+// workgroup loads all K/V tiles of its head into LDS once and then streams
+// a contiguous range of 128-query tiles past them.  The kernel is bound by
+// reading Q and writing O, so both move as whole rows: each wave DMAs its 32
+// query rows into a wave-private LDS slot (1 KB = 4 rows per instruction),
+// takes its MFMA operands from there, and stages its output rows through
+// the same slot for 16-byte-per-lane row stores.  Two slots per wave let
+// the next tile's Q stream in while the current one is computed; no
+// workgroup barrier is needed except when the head changes.
+constexpr int KVRES_SLOT = 32 * 128 * 2;   // one wave's 32 rows of Q or O at D = 128 (8 KB)
+
+template <int D, bool STAGED>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+void fa_kvres_kernel(const FaArgs a) {
+    constexpr int NW = 4, BM = 128, KS = D / 16, NDB = D / 32, NKB = BN / 32, PS = BN / 16;
+    constexpr int TILE = BN * D * 2;
+    constexpr int ROWB = D * 2;             // bytes per Q/O row
+    extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];   // [kv tile][K, V] [wave][slot]
+    LDS_AS char *const lds = (LDS_AS char *)smem_dyn;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hw = lane >> 5, l32 = lane & 31;
+    const int nkt = (a.kv_len + BN - 1) / BN;
+    LDS_AS char *const slots = lds + nkt * 2 * TILE + wave * 2 * KVRES_SLOT;
+
+    // This workgroup's items: a contiguous share of its group's range (the
+    // group is its XCD's contiguous range of items, as in fa_fwd_kernel).
+    const int g = blockIdx.x % a.groups, local = blockIdx.x / a.groups;
+    const int per_group = gridDim.x / a.groups;
+    const int i_begin = g * a.ipg + (int)((int64_t)local * a.ipg / per_group);
+    const int i_end = g * a.ipg + (int)((int64_t)(local + 1) * a.ipg / per_group);
+    if (i_begin >= i_end) return;   // uniform for the workgroup
+
+    TileCtx x;
+    x.kv_end = a.kv_len;
+    x.c = a.scale_log2;
+    x.wave = wave;
+    x.hw = hw;
+    x.k_stride = (int)(a.k_ss * 2);
+    x.v_stride = (int)(a.v_ss * 2);
+
+    LaneOffsets<D, NW> lo;
+#pragma unroll
+    for (int n = 0; n < LaneOffsets<D, NW>::PER_THREAD; ++n) {
+        const int idx = (n * NW + wave) * 64 + lane;
+        const int r = idx / (D / 8), p = idx % (D / 8);
+        lo.k_src[n] = r * x.k_stride + swz_k<D>(r, p) * 16;
+        lo.v_src[n] = r * x.v_stride + swz_v<D>(r, p) * 16;
+    }
+#pragma unroll
+    for (int k = 0; k < KS; ++k) lo.k_rd[k] = l32 * 2 * D + swz_k<D>(l32, 2 * k + hw) * 16;
+    {
+        const int li = lane & 15, gg = (lane >> 4) & 1;
+        const int r0 = 4 * hw + (li >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int col = 32 * db + 16 * gg + 4 * (li & 3);
+            lo.v_rd[db] = r0 * 2 * D + swz_v<D>(r0, col >> 3) * 16 + ((col >> 2) & 1) * 8;
+        }
+    }
+
+    // Q rows of an item for this wave: STAGED -> DMA of whole rows into a
+    // slot (row r of the 32 at r * ROWB, chunks swizzled like K); else
+    // straight into the B-operand registers.
+    auto q_rsrc = [&](int item) {
+        const int bh = item / a.n_qtiles, b = bh / a.H, hh = bh % a.H;
+        return make_rsrc(a.q + b * a.q_sb + hh * a.q_sh, ((int64_t)(a.Sq - 1) * a.q_ss + D) * 2);
+    };
+    auto q_row0 = [&](int item) { return (item % a.n_qtiles) * BM + wave * 32; };
+    auto dma_q = [&](int item, LDS_AS char *slot) {
+        const __amdgpu_buffer_rsrc_t qr = q_rsrc(item);
+        const int r0 = q_row0(item);
+#pragma unroll
+        for (int n = 0; n < 32 * (D / 8) / 64; ++n) {
+            const int idx = n * 64 + lane;              // physical chunk in the slot
+            const int r = idx / (D / 8), p = idx % (D / 8);
+            const int c = swz_k<D>(r, p);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (LDS_AS void *)(slot + n * 1024), 16,
+                                                     (int)((int64_t)(r0 + r) * a.q_ss * 2) + c * 16, 0, 0, 0);
+        }
+    };
+    auto regs_q = [&](int item, bf16x8 *qf) {
+        const __amdgpu_buffer_rsrc_t qr = q_rsrc(item);
+        const int qrow = q_row0(item) + l32;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+            qf[k] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                qr, (int)((int64_t)qrow * a.q_ss * 2) + (2 * k + hw) * 16, 0, 0));
+    };
+
+    bf16x8 qf[KS], qn[KS];
+    if (STAGED) dma_q(i_begin, slots);
+    else regs_q(i_begin, qf);
+    int cur_bh = -1;
+    for (int item = i_begin; item < i_end; ++item) {
+        const int qt = item % a.n_qtiles, bh = item / a.n_qtiles;
+        const int b = bh / a.H, hh = bh % a.H;
+        LDS_AS char *const slot = slots + ((item - i_begin) & 1) * KVRES_SLOT;
+        LDS_AS char *const next = slots + ((item - i_begin + 1) & 1) * KVRES_SLOT;
+        if (bh != cur_bh) {   // uniform: load every K/V tile of this head
+            __syncthreads();  // all waves are done with the previous head's tiles
+            x.kr = make_rsrc(a.k + b * a.k_sb + hh * a.k_sh, ((int64_t)(a.kv_len - 1) * a.k_ss + D) * 2);
+            x.vr = make_rsrc(a.v + b * a.v_sb + hh * a.v_sh, ((int64_t)(a.kv_len - 1) * a.v_ss + D) * 2);
+            for (int t = 0; t < nkt; ++t) {
+                dma_tile<D, NW>(x.kr, lo.k_src, t * BN * x.k_stride, lds + (2 * t) * TILE, wave);
+                dma_tile<D, NW>(x.vr, lo.v_src, t * BN * x.v_stride, lds + (2 * t + 1) * TILE, wave);
+            }
+            tile_barrier();   // also completes this wave's Q
+            cur_bh = bh;
+        }
+        if (STAGED) {
+            // Q of this item is in `slot` (this wave's own DMA): wait for it,
+            // read the B operand, then start the next item's Q into `next`.
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int k = 0; k < KS; ++k)
+                qf[k] = __builtin_bit_cast(bf16x8,
+                    *(const LDS_AS u32x4 *)(slot + l32 * ROWB + swz_k<D>(l32, 2 * k + hw) * 16));
+            if (item + 1 < i_end) dma_q(item + 1, next);
+        } else if (item + 1 < i_end) {
+            regs_q(item + 1, qn);
+        }
+
+        RowState<D> st;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) st.o[i] = f32x16{};
+        st.m = -1e30f;
+        st.l = 0.f;
+        for (int t = 0; t < nkt; ++t) {
+            const LDS_AS char *kt = lds + (2 * t) * TILE;
+            const LDS_AS char *vt = lds + (2 * t + 1) * TILE;
+            f32x16 sc[NKB];
+            scores<D, NW>(lo, qf, kt, sc);
+            mask_tail(x, t * BN, sc);
+            update_max<D>(x, sc, st);
+            bf16x8 pf[PS];
+            probs<D>(x, sc, st, pf);
+            accumulate_pv<D, NW>(lo, vt, pf, st);
+        }
+        const float inv = 1.0f / xhalf_sum(st.l);
+        __bf16 *obase = a.o + b * a.o_sb + hh * a.o_sh;
+        const int qrow0 = qt * BM + wave * 32;
+        if (STAGED) {
+            // O^T fragments -> row-major rows in `slot` (its Q is in registers
+            // already), then whole rows out with 16 bytes per lane.
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bf16x4 ov;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(st.o[db][i * 4 + j] * inv);
+                    const int col = 32 * db + 8 * i + 4 * hw;   // element column of ov[0]
+                    *(LDS_AS bf16x4 *)(slot + l32 * ROWB + swz_k<D>(l32, col >> 3) * 16 + (col & 7) * 2) = ov;
+                }
+#pragma unroll
+            for (int n = 0; n < 32 * (D / 8) / 64; ++n) {
+                const int idx = n * 64 + lane;
+                const int r = idx / (D / 8), c = idx % (D / 8);
+                const u32x4 w = *(const LDS_AS u32x4 *)(slot + r * ROWB + swz_k<D>(r, c) * 16);
+                if (qrow0 + r < a.Sq) *(u32x4 *)(obase + (int64_t)(qrow0 + r) * a.o_ss + c * 8) = w;
+            }
+        } else {
+            const int qrow = qrow0 + l32;
+            if (qrow < a.Sq) {
+                __bf16 *orow = obase + (int64_t)qrow * a.o_ss;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        bf16x4 ov;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(st.o[db][i * 4 + j] * inv);
+                        *(bf16x4 *)(orow + 32 * db + 8 * i + 4 * hw) = ov;
+                    }
+            }
+#pragma unroll
+            for (int k = 0; k < KS; ++k) qf[k] = qn[k];
+        }
+    }
+}
+
 // Merge the parts of one output row of a split item: M = max_r m_r,
 // L = sum_r l_r 2^(m_r - M), O = sum_r 2^(m_r - M) O_r / L, in part order.
 template <int D>
@@ -538,6 +725,7 @@ struct ltxattn_handle {
     int last_hip_error;
     // profiling
     hipEvent_t *events;
+    bool *prof_mid;   // per call and kind: was the event after the attention kernel recorded
     int prof_max, prof_n;
 };
 
@@ -581,11 +769,49 @@ int choose_nsplit(int items, int kv_len, int num_cus) {
     return ns < 1 ? 1 : ns;
 }
 
-// Launches the attention kernel (and, if some items were split, the combine
-// kernel); when `after_main` is given it is recorded between the two.
-int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len,
-                  bool split_all, hipStream_t st, hipEvent_t after_main) {
+constexpr int RESIDENT_KV_MAX = 4 * BN;   // keys held in LDS by fa_kvres_kernel (128 KB)
+constexpr size_t LDS_BYTES = 160 * 1024;  // LDS per CU on gfx950
+
+// a2v and audio self-attention: all keys resident in LDS, query tiles streamed.
+int run_resident_kv(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len, hipStream_t st) {
     const int D = h->head_dim, H = h->heads;
+    FaArgs a = {};
+    a.q = (const __bf16 *)io.q.data;
+    a.k = (const __bf16 *)io.k.data;
+    a.v = (const __bf16 *)io.v.data;
+    a.q_sb = io.q.stride_b; a.q_ss = io.q.stride_s; a.q_sh = io.q.stride_h;
+    a.k_sb = io.k.stride_b; a.k_ss = io.k.stride_s; a.k_sh = io.k.stride_h;
+    a.v_sb = io.v.stride_b; a.v_ss = io.v.stride_s; a.v_sh = io.v.stride_h;
+    a.o = (__bf16 *)io.o.data;
+    a.o_sb = io.o.stride_b; a.o_ss = io.o.stride_s; a.o_sh = io.o.stride_h;
+    a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
+    a.n_qtiles = ceil_div(Sq, 128);
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    const int items = B * H * a.n_qtiles;
+    const int nkt = ceil_div(kv_len, BN);
+    const size_t kv_lds = (size_t)nkt * 2 * BN * D * 2;
+    // Row-staged Q/O needs two 8 KB slots per wave on top of the keys.
+    const bool staged = D == 128 && kv_lds + 4 * 2 * KVRES_SLOT <= LDS_BYTES;
+    const size_t lds = kv_lds + (staged ? 4 * 2 * KVRES_SLOT : 0);
+    const int per_cu = (int)std::min<size_t>(2, LDS_BYTES / lds);   // LDS-resident workgroups per CU
+    a.groups = (items % 8 == 0 && h->num_cus % 8 == 0) ? 8 : 1;
+    a.ipg = items / a.groups;
+    const int per_group = std::min(a.ipg, per_cu * h->num_cus / a.groups);
+    a.total = a.groups * per_group;
+    if (D == 128 && staged) hipLaunchKernelGGL((fa_kvres_kernel<128, true>), dim3(a.total), dim3(256), lds, st, a);
+    else if (D == 128) hipLaunchKernelGGL((fa_kvres_kernel<128, false>), dim3(a.total), dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((fa_kvres_kernel<64, false>), dim3(a.total), dim3(256), lds, st, a);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? LTXATTN_OK : hip_fail(h, e);
+}
+
+// Launches the attention kernel and, if some items were split, the combine
+// kernel.  When `after_main` is given and a combine kernel follows, the event
+// is recorded between the two and *mid_recorded is set.
+int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len,
+                  bool split_all, hipStream_t st, hipEvent_t after_main, bool *mid_recorded) {
+    const int D = h->head_dim, H = h->heads;
+    if (!split_all && kv_len <= RESIDENT_KV_MAX) return run_resident_kv(h, io, B, Sq, kv_len, st);
     // Long query and key streams (video self-attention) take 256-query
     // workgroups: each K/V tile is then fetched once per 256 queries.  The
     // others take 128 (more workgroups for the short, memory-bound ones).
@@ -642,8 +868,11 @@ int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, i
     else hipLaunchKernelGGL((fa_fwd_kernel<64, 4>), dim3(a.total), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(h, e);
-    if (after_main && (e = hipEventRecord(after_main, st)) != hipSuccess) return hip_fail(h, e);
     if (n_split_items > 0) {
+        if (after_main) {
+            if ((e = hipEventRecord(after_main, st)) != hipSuccess) return hip_fail(h, e);
+            *mid_recorded = true;
+        }
         CombineArgs c;
         c.part_o = h->ws_o; c.part_ml = h->ws_ml;
         c.o = a.o; c.o_sb = a.o_sb; c.o_ss = a.o_ss; c.o_sh = a.o_sh;
@@ -735,6 +964,17 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
     if (g.err != hipSuccess) { g_create_hip_error = (int)g.err; free(h); return LTXATTN_ERR_HIP; }
     e = hipDeviceGetAttribute(&h->num_cus, hipDeviceAttributeMultiprocessorCount, h->device);
     if (e != hipSuccess) { g_create_hip_error = (int)e; free(h); return LTXATTN_ERR_HIP; }
+    // The resident-key kernel keeps up to RESIDENT_KV_MAX keys of K and V (and,
+    // staged, the Q/O row slots) in LDS: allow it all of a CU's LDS.
+    e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<128, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)LDS_BYTES);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<128, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<64, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)LDS_BYTES);
+    if (e != hipSuccess) { g_create_hip_error = (int)e; free(h); return LTXATTN_ERR_HIP; }
     // Workspace of the split items, BM rows per part: v2a splits every audio
     // query tile of every (batch, head) into at most NSPLIT_MAX parts; the
     // tail split of the other kinds uses at most one round of workgroups.
@@ -789,23 +1029,27 @@ int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void 
     if (g.err != hipSuccess) return hip_fail(h, g.err);
     hipStream_t st = (hipStream_t)hip_stream;
     hipEvent_t *ev = nullptr;
-    if (h->events && h->prof_n < h->prof_max) ev = h->events + (int64_t)h->prof_n++ * PROF_EVENTS;
+    bool *mid = nullptr;
+    if (h->events && h->prof_n < h->prof_max) {
+        ev = h->events + (int64_t)h->prof_n * PROF_EVENTS;
+        mid = h->prof_mid + (int64_t)h->prof_n * 4;
+        for (int n = 0; n < 4; ++n) mid[n] = false;
+        ++h->prof_n;
+    }
     hipError_t e;
     if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail(h, e);
 
     // Fixed order: video self, a2v, v2a, audio self.  For the n-th kind in
-    // that order, event 1 + 2n follows its attention kernel (before any
-    // combine kernel) and event 2 + 2n closes the kind.
+    // that order, event 2 + 2n closes the kind, and event 1 + 2n separates
+    // its attention kernel from a combine kernel if one follows.
     const int order[4] = {LTXATTN_VIDEO_SELF, LTXATTN_A2V, LTXATTN_V2A, LTXATTN_AUDIO_SELF};
     for (int n = 0; n < 4; ++n) {
         const int k = order[n];
         if (on[k]) {
             const int kv_len = (k == LTXATTN_AUDIO_SELF || k == LTXATTN_A2V) ? Lk : Sv;
             const int rc = run_attention(h, io->attn[k], B, q_rows[k], kv_len, k == LTXATTN_V2A, st,
-                                         ev ? ev[1 + 2 * n] : nullptr);
+                                         ev ? ev[1 + 2 * n] : nullptr, mid ? &mid[n] : nullptr);
             if (rc) return rc;
-        } else if (ev && (e = hipEventRecord(ev[1 + 2 * n], st)) != hipSuccess) {
-            return hip_fail(h, e);
         }
         if (ev && (e = hipEventRecord(ev[2 + 2 * n], st)) != hipSuccess) return hip_fail(h, e);
     }
@@ -818,13 +1062,22 @@ int ltxattn_profile_begin(ltxattn_handle *h, int32_t max_calls) {
     if (g.err != hipSuccess) return hip_fail(h, g.err);
     if (h->events) ltxattn_profile_end(h);
     h->events = (hipEvent_t *)calloc((size_t)max_calls * PROF_EVENTS, sizeof(hipEvent_t));
-    if (!h->events) return LTXATTN_ERR_OOM;
+    h->prof_mid = (bool *)calloc((size_t)max_calls * 4, sizeof(bool));
+    if (!h->events || !h->prof_mid) {
+        free(h->events);
+        free(h->prof_mid);
+        h->events = nullptr;
+        h->prof_mid = nullptr;
+        return LTXATTN_ERR_OOM;
+    }
     for (int64_t i = 0; i < (int64_t)max_calls * PROF_EVENTS; ++i) {
         hipError_t e = hipEventCreate(&h->events[i]);
         if (e != hipSuccess) {
             for (int64_t j = 0; j < i; ++j) (void)hipEventDestroy(h->events[j]);
             free(h->events);
+            free(h->prof_mid);
             h->events = nullptr;
+            h->prof_mid = nullptr;
             return hip_fail(h, e);
         }
     }
@@ -847,7 +1100,9 @@ int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_
         for (int s = 0; s < 4; ++s) {
             float tot = 0.f, ker = 0.f;
             if ((e = hipEventElapsedTime(&tot, ev[2 * s], ev[2 * s + 2])) != hipSuccess) return hip_fail(h, e);
-            if ((e = hipEventElapsedTime(&ker, ev[2 * s], ev[2 * s + 1])) != hipSuccess) return hip_fail(h, e);
+            const bool m = h->prof_mid[(int64_t)c * 4 + s];
+            if ((e = hipEventElapsedTime(&ker, ev[2 * s], ev[m ? 2 * s + 1 : 2 * s + 2])) != hipSuccess)
+                return hip_fail(h, e);
             out[kind_of_slot[s]] = tot;
             out[5 + kind_of_slot[s]] = ker;
         }
@@ -865,7 +1120,9 @@ int ltxattn_profile_end(ltxattn_handle *h) {
     DeviceGuard g(h->device);
     for (int64_t i = 0; i < (int64_t)h->prof_max * PROF_EVENTS; ++i) (void)hipEventDestroy(h->events[i]);
     free(h->events);
+    free(h->prof_mid);
     h->events = nullptr;
+    h->prof_mid = nullptr;
     h->prof_max = h->prof_n = 0;
     return LTXATTN_OK;
 }
