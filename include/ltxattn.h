@@ -120,11 +120,12 @@ typedef struct {
 int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out);
 
 /* Enqueue the block's attentions on hip_stream (a hipStream_t; NULL is the
- * default stream), in the fixed order VIDEO_SELF, A2V, V2A, AUDIO_SELF.
+ * default stream), in the fixed order VIDEO_SELF, V2A, A2V, AUDIO_SELF.
  * V2A runs as a split-KV pass writing fp32 partial results and softmax
  * statistics into the handle's workspace, then a combine pass that merges
- * them by log-sum-exp in a fixed order; the other kinds write bf16 O
- * directly.  Results are bit-identical from run to run.
+ * them by log-sum-exp in a fixed order (VIDEO_SELF does the same for the
+ * query tiles of an incomplete last round, when there is one); the other
+ * work writes bf16 O directly.  Results are bit-identical from run to run.
  * Errors: INVALID_ARG, UNSUPPORTED (checked before any launch), HIP. */
 int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void *hip_stream);
 

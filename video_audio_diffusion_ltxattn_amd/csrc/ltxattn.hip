@@ -186,12 +186,15 @@ struct TileCtx {
     int wave, hw;
 };
 
+// The softmax and MFMA helpers below take NK keys per call: the whole tile
+// (BN), or 32 when a tile's keys are shared out between two wave groups.
+
 // S^T = K Q^T for one tile: s[kb][i*4+j] is the score of key t0 + 32kb + 8i +
 // 4hw + j against this lane's query.
-template <int D, int NW>
+template <int D, int NW, int NK = BN>
 __device__ __forceinline__ void scores(const LaneOffsets<D, NW> &lo, const bf16x8 *qf,
                                        const LDS_AS char *__restrict__ ktile, f32x16 *s) {
-    constexpr int KS = D / 16, NKB = BN / 32;
+    constexpr int KS = D / 16, NKB = NK / 32;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
     // k outer, key block inner: the NKB accumulator chains are independent,
@@ -207,9 +210,10 @@ __device__ __forceinline__ void scores(const LaneOffsets<D, NW> &lo, const bf16x
 }
 
 // Keys at or past kv_end (ragged tail, audio padding) get -inf.
+template <int NK = BN>
 __device__ __forceinline__ void mask_tail(const TileCtx &x, int t0, f32x16 *s) {
-    constexpr int NKB = BN / 32;
-    if (t0 + BN > x.kv_end) {
+    constexpr int NKB = NK / 32;
+    if (t0 + NK > x.kv_end) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -223,9 +227,9 @@ __device__ __forceinline__ void mask_tail(const TileCtx &x, int t0, f32x16 *s) {
 // Online softmax, first half: the tile's row max, and a lazy update of the
 // max in use -- O and the row sum are rescaled only if some row's max grew
 // by more than 2^RESCALE_LOG2.
-template <int D>
+template <int D, int NK = BN>
 __device__ __forceinline__ void update_max(const TileCtx &x, const f32x16 *s, RowState<D> &st) {
-    constexpr int NDB = D / 32, NKB = BN / 32;
+    constexpr int NDB = D / 32, NKB = NK / 32;
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -252,9 +256,9 @@ __device__ __forceinline__ void update_max(const TileCtx &x, const f32x16 *s, Ro
 // {0..3} and 16k + 8 + 4hw + {0..3}, i.e. accumulator rows i = 2(k%2) and
 // 2(k%2)+1 of block k/2 -- and the row sum of exactly these bf16 weights
 // (v_dot2 with ones).
-template <int D>
+template <int D, int NK = BN>
 __device__ __forceinline__ void probs(const TileCtx &x, const f32x16 *s, RowState<D> &st, bf16x8 *pf) {
-    constexpr int PS = BN / 16;
+    constexpr int PS = NK / 16;
     const float mc = st.m * x.c;
     float rs0 = 0.f, rs1 = 0.f;
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -278,10 +282,10 @@ __device__ __forceinline__ void probs(const TileCtx &x, const f32x16 *s, RowStat
 // O^T += V^T P^T for one tile.  V^T comes from the row-major V tile via the
 // transposing read: 16 lanes read 4 key rows x 16 d, each lane ending up
 // with 4 keys of one d column.
-template <int D, int NW>
+template <int D, int NW, int NK = BN>
 __device__ __forceinline__ void accumulate_pv(const LaneOffsets<D, NW> &lo, const LDS_AS char *__restrict__ vtile,
                                               const bf16x8 *pf, RowState<D> &st) {
-    constexpr int NDB = D / 32, PS = BN / 16;
+    constexpr int NDB = D / 32, PS = NK / 16;
 #pragma unroll
     for (int k = 0; k < PS; ++k) {
 #pragma unroll
@@ -467,6 +471,237 @@ void fa_fwd_kernel(const FaArgs a) {
 }
 
 
+// ------------------------------------------------ long key streams, few queries
+// v2a: the queries of one head (the audio tokens) fit in one 128-row tile
+// while the keys (the video tokens) run to tens of thousands.  One
+// workgroup per CU streams one key range of one item through a ring of
+// STREAM_STAGES (K, V) tile pairs in LDS, waiting only for the oldest tile
+// it needs, so that two tiles stay in flight at all times (the two-buffer
+// kernel drains its loads at every step).  Its 8 waves are two groups of 4
+// (two waves per SIMD): both groups take all 128 queries, group g the keys
+// 32g..32g+31 of every tile, and the two running softmax states are merged
+// through LDS at the end.  The key-range parts of an item are merged by
+// fa_combine_kernel.
+constexpr int STREAM_STAGES = 4;
+constexpr int STREAM_NW = 8;
+
+// Wait until at most N of this wave's loads are outstanding, then meet the
+// other waves.  LDS written by a wave's loads is in place once its count
+// has dropped, so a plain s_barrier is all the other waves need; a fence
+// (as in __syncthreads) would also wait for the loads still meant to be in
+// flight.  The empty asm statements keep the compiler from moving memory
+// accesses across.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The ring, from the first loads to the last P V.  The eight stage buffers
+// are restrict parameters of this one function: the compiler then tells
+// every pending load from every LDS read and waits only where a read needs
+// a tile, which the explicit waits have already covered.  Each step, for
+// tile t whose scores are computed: wait for tile t+1 (tile t+2 may still
+// be in flight), refill the stage of tile t-1 with tile t+3 -- from a
+// zero-sized resource past the key range, so that every step issues the
+// same number of loads and the wait count stays exact -- then the scores
+// of t+1, the probabilities of t and P V of t, all on this group's 32 keys
+// (byte offset koff into a tile).
+template <int D>
+__device__ __forceinline__ void stream_ring(const TileCtx &x, const LaneOffsets<D, STREAM_NW> &lo, const bf16x8 *qf,
+                                            RowState<D> &st, int kv_begin, int ntiles, int group,
+                                            __amdgpu_buffer_rsrc_t none,
+                                            LDS_AS char *__restrict__ K0, LDS_AS char *__restrict__ K1,
+                                            LDS_AS char *__restrict__ K2, LDS_AS char *__restrict__ K3,
+                                            LDS_AS char *__restrict__ V0, LDS_AS char *__restrict__ V1,
+                                            LDS_AS char *__restrict__ V2, LDS_AS char *__restrict__ V3) {
+    constexpr int NW = STREAM_NW, NK = 32, PS = NK / 16;
+    constexpr int PER_TILE = 2 * LaneOffsets<D, NW>::PER_THREAD;   // loads per wave per tile
+    const int koff = group * NK * 2 * D, key0 = kv_begin + group * NK;
+    auto load = [&](int i, bool f, LDS_AS char *kd, LDS_AS char *vd) {
+        dma_tile<D, NW>(f ? x.kr : none, lo.k_src, (kv_begin + i * BN) * x.k_stride, kd, x.wave);
+        dma_tile<D, NW>(f ? x.vr : none, lo.v_src, (kv_begin + i * BN) * x.v_stride, vd, x.wave);
+    };
+    auto step = [&](const f32x16 *s_cur, f32x16 *s_next, int t, const LDS_AS char *k_next,
+                    const LDS_AS char *v_cur, LDS_AS char *k_fill, LDS_AS char *v_fill) {
+        ring_barrier<PER_TILE>();
+        load(t + 3, t + 3 < ntiles, k_fill, v_fill);
+        update_max<D, NK>(x, s_cur, st);
+        bf16x8 pf[PS];
+        scores<D, NW, NK>(lo, qf, k_next + koff, s_next);
+        probs<D, NK>(x, s_cur, st, pf);
+        accumulate_pv<D, NW, NK>(lo, v_cur + koff, pf, st);
+        mask_tail<NK>(x, key0 + (t + 1) * BN, s_next);
+    };
+    // Q was loaded before this: the loads complete in issue order, so the
+    // count still outstanding names exactly what has landed.
+    load(0, 0 < ntiles, K0, V0);
+    load(1, 1 < ntiles, K1, V1);
+    load(2, 2 < ntiles, K2, V2);
+    ring_barrier<2 * PER_TILE>();   // Q and tile 0
+    f32x16 sA[1], sB[1];
+    scores<D, NW, NK>(lo, qf, K0 + koff, sA);
+    mask_tail<NK>(x, key0, sA);
+    int t = 0;
+    for (; t + 4 <= ntiles; t += 4) {
+        step(sA, sB, t, K1, V0, K3, V3);
+        step(sB, sA, t + 1, K2, V1, K0, V0);
+        step(sA, sB, t + 2, K3, V2, K1, V1);
+        step(sB, sA, t + 3, K0, V3, K2, V2);
+    }
+    // 0..3 tiles left; the scores of tile t are in sA.
+    if (t < ntiles) step(sA, sB, t, K1, V0, K3, V3);
+    if (t + 1 < ntiles) step(sB, sA, t + 1, K2, V1, K0, V0);
+    if (t + 2 < ntiles) step(sA, sB, t + 2, K3, V2, K1, V1);
+    // Every wave is done with the ring, and the loads of tiles past the end
+    // have landed, before its LDS is reused.
+    ring_barrier<0>();
+}
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * STREAM_NW, 64 * STREAM_NW), amdgpu_waves_per_eu(2)))
+void fa_stream_kernel(const FaArgs a) {
+    constexpr int NW = STREAM_NW, BM = 128, KS = D / 16, NDB = D / 32, NCH = D / 8;
+    constexpr int TILE = BN * D * 2;
+    extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];   // [stage][K, V]
+    LDS_AS char *const lds = (LDS_AS char *)smem_dyn;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int group = wave >> 2, wq = wave & 3;   // key half, query block
+    const int hw = lane >> 5, l32 = lane & 31;
+
+    // Group g = XCD (blocks are dealt round-robin); within a group, item-major
+    // then part, as fa_combine_kernel expects with no whole items.
+    const int g = blockIdx.x % a.groups, local = blockIdx.x / a.groups;
+    const int part = local % a.nsplit;
+    const int item = g * a.ipg + local / a.nsplit;
+    const int qt = item % a.n_qtiles, bh = item / a.n_qtiles;
+    const int b = bh / a.H, hh = bh % a.H;
+    const int kv_begin = part * a.split_len;
+
+    TileCtx x;
+    x.kv_end = min(a.kv_len, kv_begin + a.split_len);
+    x.c = a.scale_log2;
+    x.wave = wave;
+    x.hw = hw;
+    x.k_stride = (int)(a.k_ss * 2);
+    x.v_stride = (int)(a.v_ss * 2);
+    x.kr = make_rsrc(a.k + b * a.k_sb + hh * a.k_sh, ((int64_t)(a.kv_len - 1) * a.k_ss + D) * 2);
+    x.vr = make_rsrc(a.v + b * a.v_sb + hh * a.v_sh, ((int64_t)(a.kv_len - 1) * a.v_ss + D) * 2);
+    const __amdgpu_buffer_rsrc_t none = make_rsrc(a.k, 0);
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + b * a.q_sb + hh * a.q_sh, ((int64_t)(a.Sq - 1) * a.q_ss + D) * 2);
+
+    LaneOffsets<D, NW> lo;
+#pragma unroll
+    for (int n = 0; n < LaneOffsets<D, NW>::PER_THREAD; ++n) {
+        const int idx = (n * NW + wave) * 64 + lane;
+        const int r = idx / NCH, p = idx % NCH;
+        lo.k_src[n] = r * x.k_stride + swz_k<D>(r, p) * 16;
+        lo.v_src[n] = r * x.v_stride + swz_v<D>(r, p) * 16;
+    }
+#pragma unroll
+    for (int k = 0; k < KS; ++k) lo.k_rd[k] = l32 * 2 * D + swz_k<D>(l32, 2 * k + hw) * 16;
+    {
+        const int li = lane & 15, gg = (lane >> 4) & 1;
+        const int r0 = 4 * hw + (li >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int col = 32 * db + 16 * gg + 4 * (li & 3);
+            lo.v_rd[db] = r0 * 2 * D + swz_v<D>(r0, col >> 3) * 16 + ((col >> 2) & 1) * 8;
+        }
+    }
+
+    const int qrow = qt * BM + wq * 32 + l32;
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+        qf[k] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+            qr, (int)((int64_t)qrow * a.q_ss * 2) + (2 * k + hw) * 16, 0, 0));
+    const int ntiles = (x.kv_end - kv_begin + BN - 1) / BN;
+    asm volatile("" ::: "memory");   // Q's loads stay ahead of the tiles'
+
+    RowState<D> st;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) st.o[i] = f32x16{};
+    st.m = -1e30f;
+    st.l = 0.f;
+    stream_ring<D>(x, lo, qf, st, kv_begin, ntiles, group, none,
+                   lds, lds + 2 * TILE, lds + 4 * TILE, lds + 6 * TILE,
+                   lds + TILE, lds + 3 * TILE, lds + 5 * TILE, lds + 7 * TILE);
+
+    // Merge the key halves: group 1 leaves its state in LDS (lane-major, so
+    // the partner wave of group 0 -- same queries, same lane layout -- reads
+    // exactly its own elements), group 0 folds it in and writes the result.
+    float l_tot = xhalf_sum(st.l);
+    LDS_AS char *const mo = lds + wq * (NDB * 16 * 64 * 4);                 // O, 16 floats x NDB per lane
+    LDS_AS float *const mm = (LDS_AS float *)(lds + 4 * NDB * 16 * 64 * 4) + wq * 128;   // m, l per lane
+    if (group == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = st.o[db][i * 4 + j];
+                *(LDS_AS f32x4 *)(mo + ((db * 4 + i) * 64 + lane) * 16) = v;
+            }
+        mm[lane] = st.m;
+        mm[64 + lane] = l_tot;
+    }
+    __syncthreads();
+    if (group == 1) return;
+    {
+        const float m1 = mm[lane], l1 = mm[64 + lane];
+        const float m_new = fmaxf(st.m, m1);
+        const float a0 = __builtin_amdgcn_exp2f((st.m - m_new) * x.c);
+        const float a1 = __builtin_amdgcn_exp2f((m1 - m_new) * x.c);
+        st.m = m_new;
+        l_tot = a0 * l_tot + a1 * l1;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 v = *(const LDS_AS f32x4 *)(mo + ((db * 4 + i) * 64 + lane) * 16);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) st.o[db][i * 4 + j] = a0 * st.o[db][i * 4 + j] + a1 * v[j];
+            }
+    }
+
+    if (a.nsplit == 1) {
+        if (qrow < a.Sq) {
+            const float inv = 1.0f / l_tot;
+            __bf16 *orow = a.o + b * a.o_sb + (int64_t)qrow * a.o_ss + hh * a.o_sh;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bf16x4 ov;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(st.o[db][i * 4 + j] * inv);
+                    *(bf16x4 *)(orow + 32 * db + 8 * i + 4 * hw) = ov;
+                }
+        }
+    } else {
+        const int64_t prow = ((int64_t)item * a.nsplit + part) * BM + (qrow - qt * BM);
+        float *po = a.part_o + prow * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 ov;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ov[j] = st.o[db][i * 4 + j];
+                *(f32x4 *)(po + 32 * db + 8 * i + 4 * hw) = ov;
+            }
+        if (hw == 0) {
+            a.part_ml[prow * 2 + 0] = st.m * x.c;
+            a.part_ml[prow * 2 + 1] = l_tot;
+        }
+    }
+}
+
 // ------------------------------------------------ resident short key streams
 // a2v and audio self-attention have at most a few hundred (audio) keys: a
 // workgroup loads all K/V tiles of its head into LDS once and then streams
@@ -474,15 +709,19 @@ void fa_fwd_kernel(const FaArgs a) {
 // reading Q and writing O, so both move as whole rows: each wave DMAs its 32
 // query rows into a wave-private LDS slot (1 KB = 4 rows per instruction),
 // takes its MFMA operands from there, and stages its output rows through
-// the same slot for 16-byte-per-lane row stores.  Two slots per wave let
-// the next tile's Q stream in while the current one is computed; no
-// workgroup barrier is needed except when the head changes.
+// the same slot for 16-byte-per-lane row stores.  With 4 waves per
+// workgroup each wave has two slots, so the next tile's Q streams in while
+// the current one is computed; with 8 waves (two per SIMD) each has one
+// slot and the next Q is fetched after the stores, the other wave of the
+// SIMD computing meanwhile.  No workgroup barrier is needed except when the
+// head changes.
 constexpr int KVRES_SLOT = 32 * 128 * 2;   // one wave's 32 rows of Q or O at D = 128 (8 KB)
 
-template <int D, bool STAGED>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
+template <int D, int NW, bool STAGED>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2)))
 void fa_kvres_kernel(const FaArgs a) {
-    constexpr int NW = 4, BM = 128, KS = D / 16, NDB = D / 32, NKB = BN / 32, PS = BN / 16;
+    constexpr int BM = 32 * NW, KS = D / 16, NDB = D / 32, NKB = BN / 32, PS = BN / 16;
+    constexpr int NSLOT = NW == 4 ? 2 : 1;  // Q/O row slots per wave
     constexpr int TILE = BN * D * 2;
     constexpr int ROWB = D * 2;             // bytes per Q/O row
     extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];   // [kv tile][K, V] [wave][slot]
@@ -492,7 +731,7 @@ void fa_kvres_kernel(const FaArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hw = lane >> 5, l32 = lane & 31;
     const int nkt = (a.kv_len + BN - 1) / BN;
-    LDS_AS char *const slots = lds + nkt * 2 * TILE + wave * 2 * KVRES_SLOT;
+    LDS_AS char *const slots = lds + nkt * 2 * TILE + wave * NSLOT * KVRES_SLOT;
 
     // This workgroup's items: a contiguous share of its group's range (the
     // group is its XCD's contiguous range of items, as in fa_fwd_kernel).
@@ -566,8 +805,8 @@ void fa_kvres_kernel(const FaArgs a) {
     for (int item = i_begin; item < i_end; ++item) {
         const int qt = item % a.n_qtiles, bh = item / a.n_qtiles;
         const int b = bh / a.H, hh = bh % a.H;
-        LDS_AS char *const slot = slots + ((item - i_begin) & 1) * KVRES_SLOT;
-        LDS_AS char *const next = slots + ((item - i_begin + 1) & 1) * KVRES_SLOT;
+        LDS_AS char *const slot = slots + (NSLOT == 2 ? ((item - i_begin) & 1) * KVRES_SLOT : 0);
+        LDS_AS char *const next = slots + (NSLOT == 2 ? ((item - i_begin + 1) & 1) * KVRES_SLOT : 0);
         if (bh != cur_bh) {   // uniform: load every K/V tile of this head
             __syncthreads();  // all waves are done with the previous head's tiles
             x.kr = make_rsrc(a.k + b * a.k_sb + hh * a.k_sh, ((int64_t)(a.kv_len - 1) * a.k_ss + D) * 2);
@@ -587,7 +826,7 @@ void fa_kvres_kernel(const FaArgs a) {
             for (int k = 0; k < KS; ++k)
                 qf[k] = __builtin_bit_cast(bf16x8,
                     *(const LDS_AS u32x4 *)(slot + l32 * ROWB + swz_k<D>(l32, 2 * k + hw) * 16));
-            if (item + 1 < i_end) dma_q(item + 1, next);
+            if (NSLOT == 2 && item + 1 < i_end) dma_q(item + 1, next);
         } else if (item + 1 < i_end) {
             regs_q(item + 1, qn);
         }
@@ -630,6 +869,11 @@ void fa_kvres_kernel(const FaArgs a) {
                 const int r = idx / (D / 8), c = idx % (D / 8);
                 const u32x4 w = *(const LDS_AS u32x4 *)(slot + r * ROWB + swz_k<D>(r, c) * 16);
                 if (qrow0 + r < a.Sq) *(u32x4 *)(obase + (int64_t)(qrow0 + r) * a.o_ss + c * 8) = w;
+            }
+            if (NSLOT == 1 && item + 1 < i_end) {
+                // The slot's output rows have been read (the stores hold them); refill it.
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                dma_q(item + 1, slot);
             }
         } else {
             const int qrow = qrow0 + l32;
@@ -761,14 +1005,6 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // every CU two, at least four key tiles per part, at most NSPLIT_MAX.
 constexpr int LONG_ROWS = 1024;   // query and key rows from which 8-wave workgroups are used
 
-int choose_nsplit(int items, int kv_len, int num_cus) {
-    int ns = ceil_div(2 * num_cus, items);
-    ns = ns < NSPLIT_MAX ? ns : NSPLIT_MAX;
-    const int by_len = kv_len / (4 * BN);
-    ns = ns < by_len ? ns : by_len;
-    return ns < 1 ? 1 : ns;
-}
-
 constexpr int RESIDENT_KV_MAX = 4 * BN;   // keys held in LDS by fa_kvres_kernel (128 KB)
 constexpr size_t LDS_BYTES = 160 * 1024;  // LDS per CU on gfx950
 
@@ -785,22 +1021,30 @@ int run_resident_kv(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq,
     a.o = (__bf16 *)io.o.data;
     a.o_sb = io.o.stride_b; a.o_ss = io.o.stride_s; a.o_sh = io.o.stride_h;
     a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
-    a.n_qtiles = ceil_div(Sq, 128);
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    const int items = B * H * a.n_qtiles;
     const int nkt = ceil_div(kv_len, BN);
     const size_t kv_lds = (size_t)nkt * 2 * BN * D * 2;
-    // Row-staged Q/O needs two 8 KB slots per wave on top of the keys.
-    const bool staged = D == 128 && kv_lds + 4 * 2 * KVRES_SLOT <= LDS_BYTES;
-    const size_t lds = kv_lds + (staged ? 4 * 2 * KVRES_SLOT : 0);
+    // Row-staged Q/O: 8 waves x one 8 KB slot when the keys leave room for
+    // that, else 4 waves x two slots, else unstaged (operands straight from
+    // HBM into registers).
+    int nw = 4;
+    bool staged = false;
+    if (D == 128 && kv_lds + 8 * KVRES_SLOT <= LDS_BYTES) {
+        nw = 8;
+        staged = true;
+    }
+    const size_t lds = kv_lds + (staged ? (size_t)8 * KVRES_SLOT : 0);
+    a.n_qtiles = ceil_div(Sq, 32 * nw);
+    const int items = B * H * a.n_qtiles;
     const int per_cu = (int)std::min<size_t>(2, LDS_BYTES / lds);   // LDS-resident workgroups per CU
     a.groups = (items % 8 == 0 && h->num_cus % 8 == 0) ? 8 : 1;
     a.ipg = items / a.groups;
-    const int per_group = std::min(a.ipg, per_cu * h->num_cus / a.groups);
+    const int per_group = std::min(a.ipg, (nw == 8 ? 1 : per_cu) * h->num_cus / a.groups);
     a.total = a.groups * per_group;
-    if (D == 128 && staged) hipLaunchKernelGGL((fa_kvres_kernel<128, true>), dim3(a.total), dim3(256), lds, st, a);
-    else if (D == 128) hipLaunchKernelGGL((fa_kvres_kernel<128, false>), dim3(a.total), dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((fa_kvres_kernel<64, false>), dim3(a.total), dim3(256), lds, st, a);
+    if (D == 128 && staged)
+        hipLaunchKernelGGL((fa_kvres_kernel<128, 8, true>), dim3(a.total), dim3(512), lds, st, a);
+    else if (D == 128) hipLaunchKernelGGL((fa_kvres_kernel<128, 4, false>), dim3(a.total), dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((fa_kvres_kernel<64, 4, false>), dim3(a.total), dim3(256), lds, st, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? LTXATTN_OK : hip_fail(h, e);
 }
@@ -808,10 +1052,72 @@ int run_resident_kv(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq,
 // Launches the attention kernel and, if some items were split, the combine
 // kernel.  When `after_main` is given and a combine kernel follows, the event
 // is recorded between the two and *mid_recorded is set.
+// Merge the key-range parts of n_split_items items (fa_combine_kernel).
+int run_combine(ltxattn_handle *h, const FaArgs &a, int bm, int n_split_items, hipStream_t st) {
+    CombineArgs c;
+    c.part_o = h->ws_o; c.part_ml = h->ws_ml;
+    c.o = a.o; c.o_sb = a.o_sb; c.o_ss = a.o_ss; c.o_sh = a.o_sh;
+    c.H = a.H; c.Sq = a.Sq; c.bm = bm; c.n_qtiles = a.n_qtiles; c.ipg = a.ipg; c.wpg = a.wpg;
+    c.n_split_items = n_split_items; c.nsplit = a.nsplit;
+    const int64_t threads = (int64_t)n_split_items * bm * (h->head_dim / 4);
+    const int grid = ceil_div(threads, 256);
+    if (h->head_dim == 128) hipLaunchKernelGGL((fa_combine_kernel<128>), dim3(grid), dim3(256), 0, st, c);
+    else hipLaunchKernelGGL((fa_combine_kernel<64>), dim3(grid), dim3(256), 0, st, c);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? LTXATTN_OK : hip_fail(h, e);
+}
+
+// v2a: one workgroup per CU streams one key range of one 128-query item
+// (fa_stream_kernel); as many ranges per item as fill the CUs.
+int run_stream(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len, hipStream_t st,
+               hipEvent_t after_main, bool *mid_recorded) {
+    const int D = h->head_dim, H = h->heads, BM = 128;
+    FaArgs a = {};
+    a.q = (const __bf16 *)io.q.data;
+    a.k = (const __bf16 *)io.k.data;
+    a.v = (const __bf16 *)io.v.data;
+    a.q_sb = io.q.stride_b; a.q_ss = io.q.stride_s; a.q_sh = io.q.stride_h;
+    a.k_sb = io.k.stride_b; a.k_ss = io.k.stride_s; a.k_sh = io.k.stride_h;
+    a.v_sb = io.v.stride_b; a.v_ss = io.v.stride_s; a.v_sh = io.v.stride_h;
+    a.o = (__bf16 *)io.o.data;
+    a.o_sb = io.o.stride_b; a.o_ss = io.o.stride_s; a.o_sh = io.o.stride_h;
+    a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
+    a.n_qtiles = ceil_div(Sq, BM);
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    const int items = B * H * a.n_qtiles;
+    a.groups = (items % 8 == 0 && h->num_cus % 8 == 0) ? 8 : 1;
+    a.ipg = items / a.groups;
+    a.wpg = 0;
+    int ns = h->num_cus / items;
+    ns = ns < NSPLIT_MAX ? ns : NSPLIT_MAX;
+    const int by_len = kv_len / (4 * BN);   // parts of at least 4 tiles
+    ns = ns < by_len ? ns : by_len;
+    ns = ns < 1 ? 1 : ns;
+    a.split_len = ceil_div(ceil_div(kv_len, ns), BN) * BN;
+    ns = ceil_div(kv_len, a.split_len);    // every part holds at least one key
+    a.nsplit = ns;
+    a.part_o = h->ws_o;
+    a.part_ml = h->ws_ml;
+    a.total = items * ns;
+    if (ns > 1 && (int64_t)items * ns * BM > h->ws_rows) return LTXATTN_ERR_INVALID_ARG;  // cannot happen
+    const size_t lds = (size_t)STREAM_STAGES * 2 * BN * D * 2;
+    if (D == 128) hipLaunchKernelGGL((fa_stream_kernel<128>), dim3(a.total), dim3(64 * STREAM_NW), lds, st, a);
+    else hipLaunchKernelGGL((fa_stream_kernel<64>), dim3(a.total), dim3(64 * STREAM_NW), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(h, e);
+    if (ns == 1) return LTXATTN_OK;
+    if (after_main) {
+        if ((e = hipEventRecord(after_main, st)) != hipSuccess) return hip_fail(h, e);
+        *mid_recorded = true;
+    }
+    return run_combine(h, a, BM, items, st);
+}
+
 int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len,
                   bool split_all, hipStream_t st, hipEvent_t after_main, bool *mid_recorded) {
     const int D = h->head_dim, H = h->heads;
-    if (!split_all && kv_len <= RESIDENT_KV_MAX) return run_resident_kv(h, io, B, Sq, kv_len, st);
+    if (split_all) return run_stream(h, io, B, Sq, kv_len, st, after_main, mid_recorded);
+    if (kv_len <= RESIDENT_KV_MAX) return run_resident_kv(h, io, B, Sq, kv_len, st);
     // Long query and key streams (video self-attention) take 256-query
     // workgroups: each K/V tile is then fetched once per 256 queries.  The
     // others take 128 (more workgroups for the short, memory-bound ones).
@@ -835,10 +1141,7 @@ int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, i
     const int ipg = items / groups;
     const int slots = WAVES_PER_CU / NW * h->num_cus / groups;   // workgroups resident per group
     int spg = 0, ns = 1;                                 // split items per group, parts each
-    if (split_all) {
-        ns = choose_nsplit(items, kv_len, h->num_cus);
-        if (ns > 1) spg = ipg;
-    } else if (ipg > slots) {
+    if (ipg > slots) {
         // Split the items of an incomplete last round so that it fills its XCD.
         const int rem = ipg % slots;
         if (rem > 0 && 2 * rem <= slots) {
@@ -873,20 +1176,15 @@ int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, i
             if ((e = hipEventRecord(after_main, st)) != hipSuccess) return hip_fail(h, e);
             *mid_recorded = true;
         }
-        CombineArgs c;
-        c.part_o = h->ws_o; c.part_ml = h->ws_ml;
-        c.o = a.o; c.o_sb = a.o_sb; c.o_ss = a.o_ss; c.o_sh = a.o_sh;
-        c.H = H; c.Sq = Sq; c.bm = BM; c.n_qtiles = a.n_qtiles; c.ipg = ipg; c.wpg = a.wpg;
-        c.n_split_items = n_split_items; c.nsplit = ns;
-        const int64_t threads = (int64_t)n_split_items * BM * (D / 4);
-        const int grid = ceil_div(threads, 256);
-        if (D == 128) hipLaunchKernelGGL((fa_combine_kernel<128>), dim3(grid), dim3(256), 0, st, c);
-        else hipLaunchKernelGGL((fa_combine_kernel<64>), dim3(grid), dim3(256), 0, st, c);
-        e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail(h, e);
+        return run_combine(h, a, BM, n_split_items, st);
     }
     return LTXATTN_OK;
 }
+
+// Launch order of the kinds.  v2a runs straight after video self-attention:
+// it streams the same video K and V, part of which the last-level cache
+// still holds; a2v, which writes a video-sized output, comes after it.
+constexpr int KIND_ORDER[4] = {LTXATTN_VIDEO_SELF, LTXATTN_V2A, LTXATTN_A2V, LTXATTN_AUDIO_SELF};
 
 // Argument checks shared by ltxattn_check_block and ltxattn_block_attention.
 // on[k] is set for the kinds whose output pointer is non-null.
@@ -966,14 +1264,20 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
     if (e != hipSuccess) { g_create_hip_error = (int)e; free(h); return LTXATTN_ERR_HIP; }
     // The resident-key kernel keeps up to RESIDENT_KV_MAX keys of K and V (and,
     // staged, the Q/O row slots) in LDS: allow it all of a CU's LDS.
-    e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<128, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)LDS_BYTES);
+    e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<128, 8, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
     if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<128, false>,
+        e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<128, 4, false>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
     if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<64, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)LDS_BYTES);
+        e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<64, 4, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)&fa_stream_kernel<128>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, STREAM_STAGES * 2 * BN * 128 * 2);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)&fa_stream_kernel<64>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, STREAM_STAGES * 2 * BN * 64 * 2);
     if (e != hipSuccess) { g_create_hip_error = (int)e; free(h); return LTXATTN_ERR_HIP; }
     // Workspace of the split items, BM rows per part: v2a splits every audio
     // query tile of every (batch, head) into at most NSPLIT_MAX parts; the
@@ -1039,12 +1343,11 @@ int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void 
     hipError_t e;
     if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail(h, e);
 
-    // Fixed order: video self, a2v, v2a, audio self.  For the n-th kind in
-    // that order, event 2 + 2n closes the kind, and event 1 + 2n separates
-    // its attention kernel from a combine kernel if one follows.
-    const int order[4] = {LTXATTN_VIDEO_SELF, LTXATTN_A2V, LTXATTN_V2A, LTXATTN_AUDIO_SELF};
+    // Kinds run in KIND_ORDER.  For the n-th kind in that order, event
+    // 2 + 2n closes the kind, and event 1 + 2n separates its attention
+    // kernel from a combine kernel if one follows.
     for (int n = 0; n < 4; ++n) {
-        const int k = order[n];
+        const int k = KIND_ORDER[n];
         if (on[k]) {
             const int kv_len = (k == LTXATTN_AUDIO_SELF || k == LTXATTN_A2V) ? Lk : Sv;
             const int rc = run_attention(h, io->attn[k], B, q_rows[k], kv_len, k == LTXATTN_V2A, st,
@@ -1091,7 +1394,6 @@ int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return hip_fail(h, g.err);
     const int n = h->prof_n < max_calls ? h->prof_n : max_calls;
-    const int kind_of_slot[4] = {LTXATTN_VIDEO_SELF, LTXATTN_A2V, LTXATTN_V2A, LTXATTN_AUDIO_SELF};
     for (int c = 0; c < n; ++c) {
         hipEvent_t *ev = h->events + (int64_t)c * PROF_EVENTS;
         hipError_t e = hipEventSynchronize(ev[PROF_EVENTS - 1]);
@@ -1103,8 +1405,8 @@ int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_
             const bool m = h->prof_mid[(int64_t)c * 4 + s];
             if ((e = hipEventElapsedTime(&ker, ev[2 * s], ev[m ? 2 * s + 1 : 2 * s + 2])) != hipSuccess)
                 return hip_fail(h, e);
-            out[kind_of_slot[s]] = tot;
-            out[5 + kind_of_slot[s]] = ker;
+            out[KIND_ORDER[s]] = tot;
+            out[5 + KIND_ORDER[s]] = ker;
         }
         float tot = 0.f;
         if ((e = hipEventElapsedTime(&tot, ev[0], ev[PROF_EVENTS - 1])) != hipSuccess) return hip_fail(h, e);
