@@ -182,7 +182,7 @@ def main():
                    "video_tokens": w.video_len, "audio_tokens": w.audio_kv_len,
                    "audio_buffer_rows": w.audio_len, "parallelism": "none (1 GPU)"},
         "kinds": kinds,
-        "roofline": {"kernel": "fa_fwd_kernel<128, 8> (video self-attention)",
+        "roofline": {"kernel": "fa_ring_kernel<128, 8, 1> (video self-attention)",
                      "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

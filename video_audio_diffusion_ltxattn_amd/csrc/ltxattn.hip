@@ -471,19 +471,21 @@ void fa_fwd_kernel(const FaArgs a) {
 }
 
 
-// ------------------------------------------------ long key streams, few queries
-// v2a: the queries of one head (the audio tokens) fit in one 128-row tile
-// while the keys (the video tokens) run to tens of thousands.  One
-// workgroup per CU streams one key range of one item through a ring of
-// STREAM_STAGES (K, V) tile pairs in LDS, waiting only for the oldest tile
-// it needs, so that two tiles stay in flight at all times (the two-buffer
-// kernel drains its loads at every step).  Its 8 waves are two groups of 4
-// (two waves per SIMD): both groups take all 128 queries, group g the keys
-// 32g..32g+31 of every tile, and the two running softmax states are merged
-// through LDS at the end.  The key-range parts of an item are merged by
-// fa_combine_kernel.
-constexpr int STREAM_STAGES = 4;
-constexpr int STREAM_NW = 8;
+// ------------------------------------------------ ring-pipelined streaming
+// fa_ring_kernel streams one key range of one item through a ring of
+// RING_STAGES (K, V) tile pairs in LDS and waits only for the oldest tile it
+// needs: two tiles stay in flight at all times, where fa_fwd_kernel's two
+// buffers drain their loads at every step.  One workgroup of NW waves per
+// CU (the ring takes 128 KB of LDS at D = 128).  KG = 1: every wave owns 32
+// queries (video self-attention, 256-query items).  KG = 2: v2a, whose
+// queries of one head (the audio tokens) fit in one 128-query item while
+// its keys run to tens of thousands -- the waves form two groups that both
+// take all 128 queries, group g the keys 32g..32g+31 of every tile (two
+// waves per SIMD instead of one), and the two running softmax states are
+// merged through LDS at the end.  Items, parts and the combine of split
+// items follow fa_fwd_kernel.
+constexpr int RING_STAGES = 4;
+constexpr int RING_NW = 8;
 
 // Wait until at most N of this wave's loads are outstanding, then meet the
 // other waves.  LDS written by a wave's loads is in place once its count
@@ -506,19 +508,18 @@ __device__ __forceinline__ void ring_barrier() {
 // be in flight), refill the stage of tile t-1 with tile t+3 -- from a
 // zero-sized resource past the key range, so that every step issues the
 // same number of loads and the wait count stays exact -- then the scores
-// of t+1, the probabilities of t and P V of t, all on this group's 32 keys
-// (byte offset koff into a tile).
-template <int D>
-__device__ __forceinline__ void stream_ring(const TileCtx &x, const LaneOffsets<D, STREAM_NW> &lo, const bf16x8 *qf,
-                                            RowState<D> &st, int kv_begin, int ntiles, int group,
-                                            __amdgpu_buffer_rsrc_t none,
-                                            LDS_AS char *__restrict__ K0, LDS_AS char *__restrict__ K1,
-                                            LDS_AS char *__restrict__ K2, LDS_AS char *__restrict__ K3,
-                                            LDS_AS char *__restrict__ V0, LDS_AS char *__restrict__ V1,
-                                            LDS_AS char *__restrict__ V2, LDS_AS char *__restrict__ V3) {
-    constexpr int NW = STREAM_NW, NK = 32, PS = NK / 16;
+// of t+1, the probabilities of t and P V of t, on this wave's NK keys of
+// each tile (starting koff bytes into it).
+template <int D, int NW, int NK>
+__device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D, NW> &lo, const bf16x8 *qf,
+                                          RowState<D> &st, int kv_begin, int ntiles, int koff, int key0,
+                                          __amdgpu_buffer_rsrc_t none,
+                                          LDS_AS char *__restrict__ K0, LDS_AS char *__restrict__ K1,
+                                          LDS_AS char *__restrict__ K2, LDS_AS char *__restrict__ K3,
+                                          LDS_AS char *__restrict__ V0, LDS_AS char *__restrict__ V1,
+                                          LDS_AS char *__restrict__ V2, LDS_AS char *__restrict__ V3) {
+    constexpr int NKB = NK / 32, PS = NK / 16;
     constexpr int PER_TILE = 2 * LaneOffsets<D, NW>::PER_THREAD;   // loads per wave per tile
-    const int koff = group * NK * 2 * D, key0 = kv_begin + group * NK;
     auto load = [&](int i, bool f, LDS_AS char *kd, LDS_AS char *vd) {
         dma_tile<D, NW>(f ? x.kr : none, lo.k_src, (kv_begin + i * BN) * x.k_stride, kd, x.wave);
         dma_tile<D, NW>(f ? x.vr : none, lo.v_src, (kv_begin + i * BN) * x.v_stride, vd, x.wave);
@@ -540,7 +541,7 @@ __device__ __forceinline__ void stream_ring(const TileCtx &x, const LaneOffsets<
     load(1, 1 < ntiles, K1, V1);
     load(2, 2 < ntiles, K2, V2);
     ring_barrier<2 * PER_TILE>();   // Q and tile 0
-    f32x16 sA[1], sB[1];
+    f32x16 sA[NKB], sB[NKB];
     scores<D, NW, NK>(lo, qf, K0 + koff, sA);
     mask_tail<NK>(x, key0, sA);
     int t = 0;
@@ -555,34 +556,42 @@ __device__ __forceinline__ void stream_ring(const TileCtx &x, const LaneOffsets<
     if (t + 1 < ntiles) step(sB, sA, t + 1, K2, V1, K0, V0);
     if (t + 2 < ntiles) step(sA, sB, t + 2, K3, V2, K1, V1);
     // Every wave is done with the ring, and the loads of tiles past the end
-    // have landed, before its LDS is reused.
+    // have landed, before its LDS is reused or released.
     ring_barrier<0>();
 }
 
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * STREAM_NW, 64 * STREAM_NW), amdgpu_waves_per_eu(2)))
-void fa_stream_kernel(const FaArgs a) {
-    constexpr int NW = STREAM_NW, BM = 128, KS = D / 16, NDB = D / 32, NCH = D / 8;
+template <int D, int NW, int KG>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2)))
+void fa_ring_kernel(const FaArgs a) {
+    constexpr int QW = NW / KG;                 // waves per key group = 32-query blocks per item
+    constexpr int BM = 32 * QW, NK = BN / KG;
+    constexpr int KS = D / 16, NDB = D / 32, NCH = D / 8;
     constexpr int TILE = BN * D * 2;
-    extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];   // [stage][K, V]
+    // K stages 0..3, then V stages 0..3: each kind's reads then reach all
+    // its stages by immediate offsets (< 64 KB) from one address per lane.
+    extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];
     LDS_AS char *const lds = (LDS_AS char *)smem_dyn;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int group = wave >> 2, wq = wave & 3;   // key half, query block
+    const int group = wave / QW, wq = wave % QW;
     const int hw = lane >> 5, l32 = lane & 31;
 
-    // Group g = XCD (blocks are dealt round-robin); within a group, item-major
-    // then part, as fa_combine_kernel expects with no whole items.
-    const int g = blockIdx.x % a.groups, local = blockIdx.x / a.groups;
-    const int part = local % a.nsplit;
-    const int item = g * a.ipg + local / a.nsplit;
+    // Item decode as in fa_fwd_kernel: group g = XCD; whole items first,
+    // then the parts of the split items.
+    const int bid = blockIdx.x;
+    const int g = bid % a.groups, local = bid / a.groups;
+    const bool split_item = local >= a.wpg;
+    const int w = local - a.wpg;
+    const int part = split_item ? w % a.nsplit : 0;
+    const int item = g * a.ipg + (split_item ? a.wpg + w / a.nsplit : local);
+    const int split_idx = g * (a.ipg - a.wpg) + (split_item ? w / a.nsplit : 0);
     const int qt = item % a.n_qtiles, bh = item / a.n_qtiles;
     const int b = bh / a.H, hh = bh % a.H;
     const int kv_begin = part * a.split_len;
 
     TileCtx x;
-    x.kv_end = min(a.kv_len, kv_begin + a.split_len);
+    x.kv_end = split_item ? min(a.kv_len, kv_begin + a.split_len) : a.kv_len;
     x.c = a.scale_log2;
     x.wave = wave;
     x.hw = hw;
@@ -627,32 +636,32 @@ void fa_stream_kernel(const FaArgs a) {
     for (int i = 0; i < NDB; ++i) st.o[i] = f32x16{};
     st.m = -1e30f;
     st.l = 0.f;
-    stream_ring<D>(x, lo, qf, st, kv_begin, ntiles, group, none,
-                   lds, lds + 2 * TILE, lds + 4 * TILE, lds + 6 * TILE,
-                   lds + TILE, lds + 3 * TILE, lds + 5 * TILE, lds + 7 * TILE);
+    ring_loop<D, NW, NK>(x, lo, qf, st, kv_begin, ntiles, group * NK * 2 * D, kv_begin + group * NK, none,
+                         lds, lds + TILE, lds + 2 * TILE, lds + 3 * TILE,
+                         lds + 4 * TILE, lds + 5 * TILE, lds + 6 * TILE, lds + 7 * TILE);
 
-    // Merge the key halves: group 1 leaves its state in LDS (lane-major, so
-    // the partner wave of group 0 -- same queries, same lane layout -- reads
-    // exactly its own elements), group 0 folds it in and writes the result.
     float l_tot = xhalf_sum(st.l);
-    LDS_AS char *const mo = lds + wq * (NDB * 16 * 64 * 4);                 // O, 16 floats x NDB per lane
-    LDS_AS float *const mm = (LDS_AS float *)(lds + 4 * NDB * 16 * 64 * 4) + wq * 128;   // m, l per lane
-    if (group == 1) {
+    if (KG == 2) {
+        // Merge the key halves: group 1 leaves its state in LDS (lane-major,
+        // so the partner wave of group 0 -- same queries, same lane layout --
+        // reads exactly its own elements), group 0 folds it in.
+        LDS_AS char *const mo = lds + wq * (NDB * 16 * 64 * 4);
+        LDS_AS float *const mm = (LDS_AS float *)(lds + QW * NDB * 16 * 64 * 4) + wq * 128;
+        if (group == 1) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4 v;
+                for (int i = 0; i < 4; ++i) {
+                    f32x4 v;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = st.o[db][i * 4 + j];
-                *(LDS_AS f32x4 *)(mo + ((db * 4 + i) * 64 + lane) * 16) = v;
-            }
-        mm[lane] = st.m;
-        mm[64 + lane] = l_tot;
-    }
-    __syncthreads();
-    if (group == 1) return;
-    {
+                    for (int j = 0; j < 4; ++j) v[j] = st.o[db][i * 4 + j];
+                    *(LDS_AS f32x4 *)(mo + ((db * 4 + i) * 64 + lane) * 16) = v;
+                }
+            mm[lane] = st.m;
+            mm[64 + lane] = l_tot;
+        }
+        __syncthreads();
+        if (group == 1) return;
         const float m1 = mm[lane], l1 = mm[64 + lane];
         const float m_new = fmaxf(st.m, m1);
         const float a0 = __builtin_amdgcn_exp2f((st.m - m_new) * x.c);
@@ -669,7 +678,8 @@ void fa_stream_kernel(const FaArgs a) {
             }
     }
 
-    if (a.nsplit == 1) {
+    // st.o[db][i*4+j] is O^T[d = 32db + 8i + 4hw + j][query qrow] (unnormalised).
+    if (!split_item) {
         if (qrow < a.Sq) {
             const float inv = 1.0f / l_tot;
             __bf16 *orow = a.o + b * a.o_sb + (int64_t)qrow * a.o_ss + hh * a.o_sh;
@@ -684,7 +694,7 @@ void fa_stream_kernel(const FaArgs a) {
                 }
         }
     } else {
-        const int64_t prow = ((int64_t)item * a.nsplit + part) * BM + (qrow - qt * BM);
+        const int64_t prow = ((int64_t)split_idx * a.nsplit + part) * BM + (qrow - qt * BM);
         float *po = a.part_o + prow * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -1068,7 +1078,7 @@ int run_combine(ltxattn_handle *h, const FaArgs &a, int bm, int n_split_items, h
 }
 
 // v2a: one workgroup per CU streams one key range of one 128-query item
-// (fa_stream_kernel); as many ranges per item as fill the CUs.
+// (fa_ring_kernel with two key groups); as many ranges per item as fill the CUs.
 int run_stream(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len, hipStream_t st,
                hipEvent_t after_main, bool *mid_recorded) {
     const int D = h->head_dim, H = h->heads, BM = 128;
@@ -1087,7 +1097,6 @@ int run_stream(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int 
     const int items = B * H * a.n_qtiles;
     a.groups = (items % 8 == 0 && h->num_cus % 8 == 0) ? 8 : 1;
     a.ipg = items / a.groups;
-    a.wpg = 0;
     int ns = h->num_cus / items;
     ns = ns < NSPLIT_MAX ? ns : NSPLIT_MAX;
     const int by_len = kv_len / (4 * BN);   // parts of at least 4 tiles
@@ -1096,13 +1105,14 @@ int run_stream(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int 
     a.split_len = ceil_div(ceil_div(kv_len, ns), BN) * BN;
     ns = ceil_div(kv_len, a.split_len);    // every part holds at least one key
     a.nsplit = ns;
+    a.wpg = ns == 1 ? a.ipg : 0;           // one part: every item is whole
     a.part_o = h->ws_o;
     a.part_ml = h->ws_ml;
     a.total = items * ns;
     if (ns > 1 && (int64_t)items * ns * BM > h->ws_rows) return LTXATTN_ERR_INVALID_ARG;  // cannot happen
-    const size_t lds = (size_t)STREAM_STAGES * 2 * BN * D * 2;
-    if (D == 128) hipLaunchKernelGGL((fa_stream_kernel<128>), dim3(a.total), dim3(64 * STREAM_NW), lds, st, a);
-    else hipLaunchKernelGGL((fa_stream_kernel<64>), dim3(a.total), dim3(64 * STREAM_NW), lds, st, a);
+    const size_t lds = (size_t)RING_STAGES * 2 * BN * D * 2;
+    if (D == 128) hipLaunchKernelGGL((fa_ring_kernel<128, RING_NW, 2>), dim3(a.total), dim3(64 * RING_NW), lds, st, a);
+    else hipLaunchKernelGGL((fa_ring_kernel<64, RING_NW, 2>), dim3(a.total), dim3(64 * RING_NW), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(h, e);
     if (ns == 1) return LTXATTN_OK;
@@ -1166,7 +1176,9 @@ int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, i
     const int n_split_items = groups * spg;
     if ((int64_t)n_split_items * ns * BM > h->ws_rows) return LTXATTN_ERR_INVALID_ARG;  // cannot happen
 
-    if (D == 128 && NW == 8) hipLaunchKernelGGL((fa_fwd_kernel<128, 8>), dim3(a.total), dim3(512), 0, st, a);
+    if (D == 128 && NW == 8)
+        hipLaunchKernelGGL((fa_ring_kernel<128, RING_NW, 1>), dim3(a.total), dim3(64 * RING_NW),
+                           (size_t)RING_STAGES * 2 * BN * 128 * 2, st, a);
     else if (D == 128) hipLaunchKernelGGL((fa_fwd_kernel<128, 4>), dim3(a.total), dim3(256), 0, st, a);
     else hipLaunchKernelGGL((fa_fwd_kernel<64, 4>), dim3(a.total), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
@@ -1273,11 +1285,14 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
         e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<64, 4, false>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
     if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_stream_kernel<128>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, STREAM_STAGES * 2 * BN * 128 * 2);
+        e = hipFuncSetAttribute((const void *)&fa_ring_kernel<128, RING_NW, 2>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 128 * 2);
     if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_stream_kernel<64>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, STREAM_STAGES * 2 * BN * 64 * 2);
+        e = hipFuncSetAttribute((const void *)&fa_ring_kernel<64, RING_NW, 2>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 64 * 2);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)&fa_ring_kernel<128, RING_NW, 1>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 128 * 2);
     if (e != hipSuccess) { g_create_hip_error = (int)e; free(h); return LTXATTN_ERR_HIP; }
     // Workspace of the split items, BM rows per part: v2a splits every audio
     // query tile of every (batch, head) into at most NSPLIT_MAX parts; the
