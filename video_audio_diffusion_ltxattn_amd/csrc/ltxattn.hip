@@ -510,7 +510,7 @@ __device__ __forceinline__ void ring_barrier() {
 // same number of loads and the wait count stays exact -- then the scores
 // of t+1, the probabilities of t and P V of t, on this wave's NK keys of
 // each tile (starting koff bytes into it).
-template <int D, int NW, int NK>
+template <int D, int NW, int NK, bool SW = true>
 __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D, NW> &lo, const bf16x8 *qf,
                                           RowState<D> &st, int kv_begin, int ntiles, int koff, int key0,
                                           __amdgpu_buffer_rsrc_t none,
@@ -524,16 +524,109 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
         dma_tile<D, NW>(f ? x.kr : none, lo.k_src, (kv_begin + i * BN) * x.k_stride, kd, x.wave);
         dma_tile<D, NW>(f ? x.vr : none, lo.v_src, (kv_begin + i * BN) * x.v_stride, vd, x.wave);
     };
-    auto step = [&](const f32x16 *s_cur, f32x16 *s_next, int t, const LDS_AS char *k_next,
-                    const LDS_AS char *v_cur, LDS_AS char *k_fill, LDS_AS char *v_fill) {
+    // Software-pipelined step (NK = BN = 64, D = 128): phase A interleaves
+    // the 16 score MFMAs of tile t+1 (K operands read one k-step ahead) with
+    // the exponentials of tile t; phase B interleaves the 16 P V MFMAs of
+    // tile t (V operands read one chunk ahead) with the row max of tile t+1,
+    // whose rescale decision closes the step.
+    auto step_sw = [&](const f32x16 *s_cur, f32x16 *s_next, int t, const LDS_AS char *k_next,
+                       const LDS_AS char *v_cur, LDS_AS char *k_fill, LDS_AS char *v_fill) {
+        constexpr int KS = D / 16, NDB = D / 32;
         ring_barrier<PER_TILE>();
         load(t + 3, t + 3 < ntiles, k_fill, v_fill);
-        update_max<D, NK>(x, s_cur, st);
         bf16x8 pf[PS];
-        scores<D, NW, NK>(lo, qf, k_next + koff, s_next);
-        probs<D, NK>(x, s_cur, st, pf);
-        accumulate_pv<D, NW, NK>(lo, v_cur + koff, pf, st);
+        bf16x8 kop[2][NKB];
+        float rs0 = 0.f, rs1 = 0.f;
+        const float mc = st.m * x.c;
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        auto read_k = [&](int k, bf16x8 *op) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                op[kb] = __builtin_bit_cast(bf16x8, *(const LDS_AS u32x4 *)(k_next + koff + kb * 32 * 2 * D + lo.k_rd[k]));
+        };
+        read_k(0, kop[0]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < KS; ++c) {
+            if (c + 1 < KS) read_k(c + 1, kop[(c + 1) & 1]);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c & 1][kb], qf[c],
+                                                                     c == 0 ? f32x16{} : s_next[kb], 0, 0, 0);
+            if (c < PS) {   // exponentials of P k-step c
+                const int kb = c >> 1, i0 = 2 * (c & 1);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pf[c][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][i0 * 4 + j], x.c, -mc));
+                    pf[c][4 + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][(i0 + 1) * 4 + j], x.c, -mc));
+                }
+#pragma unroll
+                for (int j = 0; j < 8; j += 4) {
+                    rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[c][j], pf[c][j + 1]}, one, rs0, false);
+                    rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[c][j + 2], pf[c][j + 3]}, one, rs1, false);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        st.l += rs0 + rs1;
         mask_tail<NK>(x, key0 + (t + 1) * BN, s_next);
+        bf16x8 vop[2][2];
+        auto read_v = [&](int c, bf16x8 *op) {   // chunk c: k-step c/2, d blocks 2(c%2), 2(c%2)+1
+            const int k = c >> 1, dbp = c & 1;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const LDS_AS char *vp = v_cur + koff + lo.v_rd[2 * dbp + j] + k * 16 * 2 * D;
+                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)vp);
+                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vp + 8 * 2 * D));
+                op[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        };
+        float mx0 = -INFINITY, mx1 = -INFINITY;
+        read_v(0, vop[0]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < 2 * PS; ++c) {
+            if (c + 1 < 2 * PS) read_v(c + 1, vop[(c + 1) & 1]);
+            const int k = c >> 1, dbp = c & 1;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                st.o[2 * dbp + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[c & 1][j], pf[k], st.o[2 * dbp + j], 0, 0, 0);
+            if (c >= 2 && c < 6) {   // a quarter of the row max of tile t+1
+                const int q4 = c - 2, kb = q4 >> 1, e0 = 8 * (q4 & 1);
+#pragma unroll
+                for (int e = e0; e < e0 + 8; e += 4) {
+                    mx0 = fmaxf(fmaxf(mx0, s_next[kb][e]), s_next[kb][e + 1]);
+                    mx1 = fmaxf(fmaxf(mx1, s_next[kb][e + 2]), s_next[kb][e + 3]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const float m_t = xhalf_max(fmaxf(mx0, mx1));
+        if (__builtin_amdgcn_ballot_w64((m_t - st.m) * x.c > RESCALE_LOG2)) {
+            const float m_new = fmaxf(st.m, m_t);
+            const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * x.c);
+            st.m = m_new;
+            st.l *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
+        }
+    };
+    auto step = [&](const f32x16 *s_cur, f32x16 *s_next, int t, const LDS_AS char *k_next,
+                    const LDS_AS char *v_cur, LDS_AS char *k_fill, LDS_AS char *v_fill) {
+        if constexpr (SW && NK == BN && D == 128) {
+            step_sw(s_cur, s_next, t, k_next, v_cur, k_fill, v_fill);
+        } else {
+            ring_barrier<PER_TILE>();
+            load(t + 3, t + 3 < ntiles, k_fill, v_fill);
+            update_max<D, NK>(x, s_cur, st);
+            bf16x8 pf[PS];
+            scores<D, NW, NK>(lo, qf, k_next + koff, s_next);
+            probs<D, NK>(x, s_cur, st, pf);
+            accumulate_pv<D, NW, NK>(lo, v_cur + koff, pf, st);
+            mask_tail<NK>(x, key0 + (t + 1) * BN, s_next);
+        }
     };
     // Q was loaded before this: the loads complete in issue order, so the
     // count still outstanding names exactly what has landed.
@@ -544,6 +637,7 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
     f32x16 sA[NKB], sB[NKB];
     scores<D, NW, NK>(lo, qf, K0 + koff, sA);
     mask_tail<NK>(x, key0, sA);
+    if constexpr (SW && NK == BN && D == 128) update_max<D, NK>(x, sA, st);   // steps expect it settled
     int t = 0;
     for (; t + 4 <= ntiles; t += 4) {
         step(sA, sB, t, K1, V0, K3, V3);
