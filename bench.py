@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark: attention TFLOP/s of one LTX-2 DiT block's attention set on one MI355X.
 
-A step is one ``ltxattn_block_attention`` call -- video self-attention, a2v,
-v2a (split-KV pass + combine) and audio self-attention -- over the
+A step is one ``ltxattn_block_attention`` call -- video self-attention, v2a
+(key-range pass + combine), a2v and audio self-attention -- over the
 768x1280x121 clip: 15360 video tokens, 126 audio tokens padded to 128, 32
 heads of 128, batch 1 (TensorRT-LLM PR #16228, "Description").  Inputs are
 seeded synthetic bf16 tensors already resident in HBM.

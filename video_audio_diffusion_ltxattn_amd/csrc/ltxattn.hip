@@ -525,17 +525,19 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
         dma_tile<D, NW>(f ? x.vr : none, lo.v_src, (kv_begin + i * BN) * x.v_stride, vd, x.wave);
     };
     // Software-pipelined step (NK = BN = 64, D = 128): phase A interleaves
-    // the 16 score MFMAs of tile t+1 (K operands read one k-step ahead) with
-    // the exponentials of tile t; phase B interleaves the 16 P V MFMAs of
-    // tile t (V operands read one chunk ahead) with the row max of tile t+1,
-    // whose rescale decision closes the step.
+    // the 16 score MFMAs of tile t+1, two per k-step, with the exponentials
+    // of tile t, four per k-step; phase B interleaves the 16 P V MFMAs of
+    // tile t with the row max of tile t+1, whose rescale decision closes the
+    // step.  Operand reads run two chunks ahead; the scheduling barriers
+    // keep this order.
     auto step_sw = [&](const f32x16 *s_cur, f32x16 *s_next, int t, const LDS_AS char *k_next,
                        const LDS_AS char *v_cur, LDS_AS char *k_fill, LDS_AS char *v_fill) {
         constexpr int KS = D / 16, NDB = D / 32;
         ring_barrier<PER_TILE>();
         load(t + 3, t + 3 < ntiles, k_fill, v_fill);
         bf16x8 pf[PS];
-        bf16x8 kop[2][NKB];
+        constexpr int LA = 2;   // operand reads run LA chunks ahead of their MFMAs
+        bf16x8 kop[LA + 1][NKB];
         float rs0 = 0.f, rs1 = 0.f;
         const float mc = st.m * x.c;
         const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -544,34 +546,30 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
             for (int kb = 0; kb < NKB; ++kb)
                 op[kb] = __builtin_bit_cast(bf16x8, *(const LDS_AS u32x4 *)(k_next + koff + kb * 32 * 2 * D + lo.k_rd[k]));
         };
-        read_k(0, kop[0]);
+#pragma unroll
+        for (int c = 0; c < LA; ++c) read_k(c, kop[c]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < KS; ++c) {
-            if (c + 1 < KS) read_k(c + 1, kop[(c + 1) & 1]);
+            if (c + LA < KS) read_k(c + LA, kop[(c + LA) % (LA + 1)]);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
-                s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c & 1][kb], qf[c],
+                s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c % (LA + 1)][kb], qf[c],
                                                                      c == 0 ? f32x16{} : s_next[kb], 0, 0, 0);
-            if (c < PS) {   // exponentials of P k-step c
-                const int kb = c >> 1, i0 = 2 * (c & 1);
+            {   // half (c & 1) of the exponentials of P k-step c / 2
+                const int k = c >> 1, h = c & 1, kb = k >> 1, i = 2 * (k & 1) + h;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pf[c][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][i0 * 4 + j], x.c, -mc));
-                    pf[c][4 + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][(i0 + 1) * 4 + j], x.c, -mc));
-                }
-#pragma unroll
-                for (int j = 0; j < 8; j += 4) {
-                    rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[c][j], pf[c][j + 1]}, one, rs0, false);
-                    rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[c][j + 2], pf[c][j + 3]}, one, rs1, false);
-                }
+                for (int j = 0; j < 4; ++j)
+                    pf[k][4 * h + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][i * 4 + j], x.c, -mc));
+                rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][4 * h], pf[k][4 * h + 1]}, one, rs0, false);
+                rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][4 * h + 2], pf[k][4 * h + 3]}, one, rs1, false);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         st.l += rs0 + rs1;
         mask_tail<NK>(x, key0 + (t + 1) * BN, s_next);
-        bf16x8 vop[2][2];
-        auto read_v = [&](int c, bf16x8 *op) {   // chunk c: k-step c/2, d blocks 2(c%2), 2(c%2)+1
+        bf16x8 vop[LA + 1][2];
+        auto read_v = [&](int c, bf16x8 *op) {
             const int k = c >> 1, dbp = c & 1;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -582,15 +580,16 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
             }
         };
         float mx0 = -INFINITY, mx1 = -INFINITY;
-        read_v(0, vop[0]);
+#pragma unroll
+        for (int c = 0; c < LA; ++c) read_v(c, vop[c]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < 2 * PS; ++c) {
-            if (c + 1 < 2 * PS) read_v(c + 1, vop[(c + 1) & 1]);
+            if (c + LA < 2 * PS) read_v(c + LA, vop[(c + LA) % (LA + 1)]);
             const int k = c >> 1, dbp = c & 1;
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                st.o[2 * dbp + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[c & 1][j], pf[k], st.o[2 * dbp + j], 0, 0, 0);
+                st.o[2 * dbp + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[c % (LA + 1)][j], pf[k], st.o[2 * dbp + j], 0, 0, 0);
             if (c >= 2 && c < 6) {   // a quarter of the row max of tile t+1
                 const int q4 = c - 2, kb = q4 >> 1, e0 = 8 * (q4 & 1);
 #pragma unroll
