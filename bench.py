@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -40,8 +41,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_video_self_15360.json")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source's code: comments, blank lines and
+    trailing blanks are dropped, so only a change of code invalidates the
+    counters taken on it."""
+    with open(KERNEL_SRC) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def measured_traffic():

@@ -9,10 +9,8 @@
 // accumulation and fp32 softmax statistics.
 //
 // Kernel design (gfx950, 64-wide waves):
-//  * Each wave owns 32 query rows; a workgroup of NW = 8 waves (video
-//    self-attention) or 4 waves (the rest) covers BM = 32 * NW query rows of
-//    one (batch, head), and every K/V tile it loads serves all of them.
-//    Keys stream through in tiles of BN = 64.
+//  * Each wave owns 32 query rows of one (batch, head); keys stream through
+//    in tiles of BN = 64.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K is the A operand (from LDS) and Q^T the B
 //    operand (held in registers for the whole kernel).  In the 32x32
@@ -27,28 +25,35 @@
 //    permuted freely, the key order the score accumulator happens to give
 //    each half-wave is simply used for V as well.
 //  * K and V tiles go HBM -> LDS with buffer_load ... lds (no VGPR
-//    staging), double-buffered.  K runs one tile ahead of V: while the
-//    softmax of tile t runs on the VALU, the MFMAs compute the scores of
-//    tile t+1.  Buffer range checks return zeros for rows past the valid
+//    staging).  Buffer range checks return zeros for rows past the valid
 //    length, which handles ragged tails and the audio key padding without
-//    branches; the padded keys are never read.
-//  * LDS rows are XOR-swizzled per tensor so the K reads (ds_read_b128, 16
-//    rows per pass) and the transposed V reads (4 rows per pass) are free
-//    of bank conflicts.
+//    branches; the padded keys are never read.  LDS rows are XOR-swizzled
+//    per tensor so the K reads (16 rows per pass) and the transposed V
+//    reads (4 rows per pass) are free of bank conflicts.
 //  * Workgroups are remapped so that each of the 8 XCDs works through a
-//    contiguous range of (batch, head) slices and the K/V of a head stay
-//    in that XCD's L2.
-//  * A work item is one (batch, head, 128-query tile).  Items can be split
-//    over the key range: each part writes an unnormalised fp32 partial O
-//    plus its row max and row sum, and a combine kernel merges the parts by
-//    log-sum-exp in a fixed order (the same softmax statistics merge that
-//    the context-parallel v2a of TensorRT-Model-Connect PR #1586 does
-//    across ranks).  v2a (126..256 audio queries per head against
-//    15360..27280 video keys) splits every item so the latency-bound audio
-//    side fills the chip.  Video self-attention splits only the items of an
-//    incomplete last round of workgroups: with 2 resident workgroups per CU,
-//    3840 items would leave the 8th round half empty, so the last 256 items
-//    run as 512 half-length parts instead.
+//    contiguous range of items and the K/V of a head stay in its L2.
+//  * Items can be split over the key range: each part writes an
+//    unnormalised fp32 partial O plus its row max and row sum, and a
+//    combine kernel merges the parts by log-sum-exp in a fixed order (the
+//    softmax statistics merge that the context-parallel v2a of
+//    TensorRT-Model-Connect PR #1586 does across ranks).
+//  * Kernels per kind (one block call launches them in this order):
+//      video self   fa_ring_kernel<D, 8, 1>: 256-query items, one 8-wave
+//                   workgroup per CU, a 4-stage K/V ring in LDS with
+//                   partial load waits, a software-pipelined step (score
+//                   MFMAs of tile t+1 interleaved with the exponentials of
+//                   tile t).  The items of an incomplete last round run as
+//                   key-range halves so the round fills its XCD.
+//      v2a          fa_ring_kernel<D, 8, 2>: every 128-query item (all the
+//                   audio queries of a head) split over the video keys, one
+//                   part per CU; two 4-wave groups take the two key halves
+//                   of each tile and merge in LDS; then fa_combine_kernel.
+//      a2v, audio   fa_kvres_kernel: the few hundred audio keys of a head
+//      self         stay in LDS while the query tiles stream past; Q and O
+//                   move as whole rows through per-wave LDS slots.
+//      other shapes fa_fwd_kernel<D, 4> (two-buffer pipeline, 128-query
+//                   items) for long key streams that the cases above do
+//                   not cover, e.g. D = 64 or short video.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
