@@ -61,6 +61,12 @@ RAGGED = [
     synth.Workload(15, "whole tiles", 1, 2, 128, 128, 64, 64),
     # scaled keys, spike
     synth.Workload(16, "spiky", 1, 2, 128, 700, 96, 90, k_scale=0.5, spike_rank=4, spike_amp=3.0),
+    # Video self-attention on the 256-query ring kernel with a ragged last
+    # query tile and a ragged last key tile; the ring's 4-step unroll leaves
+    # 2, 3 and 1 tiles over (18, 19 and 17 key tiles).  v2a parts of 3..5 tiles.
+    synth.Workload(17, "ring ragged", 2, 2, 128, 1100, 77, 70),
+    synth.Workload(18, "ring remainder 3", 1, 1, 128, 1215, 130, 129),
+    synth.Workload(19, "ring remainder 1", 1, 3, 128, 1030, 16, 16),
 ]
 
 
@@ -111,10 +117,11 @@ def test_full_size_sampled(lt, torch, cfg):
 
 
 def test_tail_round_split(lt, torch):
-    """8 heads x 9216 video queries = 576 work items of 128 queries.  On a
-    256-CU MI355X each XCD's group holds one head's 72 items; with 2 resident
-    workgroups per CU the last 8 query tiles of each head run as key-range
-    parts merged by the combine kernel.  Rows there and elsewhere must match."""
+    """8 heads x 9216 video queries = 288 work items of 256 queries.  On a
+    256-CU MI355X each XCD's group holds one head's 36 items and runs 32 at a
+    time, so the last 4 query tiles of each head (rows 8192..9215) run as
+    key-range parts merged by the combine kernel.  Rows there and elsewhere
+    must match."""
     w = synth.Workload(31, "tail split", 1, 8, 128, 9216, 64, 64)
     inputs = synth.make_block_inputs(w)
     got = run_block(lt, torch, w, inputs, kinds=("video_self",))
