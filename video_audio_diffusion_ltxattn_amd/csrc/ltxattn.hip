@@ -1157,9 +1157,6 @@ int run_resident_kv(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq,
     return e == hipSuccess ? LTXATTN_OK : hip_fail(h, e);
 }
 
-// Launches the attention kernel and, if some items were split, the combine
-// kernel.  When `after_main` is given and a combine kernel follows, the event
-// is recorded between the two and *mid_recorded is set.
 // Merge the key-range parts of n_split_items items (fa_combine_kernel).
 int run_combine(ltxattn_handle *h, const FaArgs &a, int bm, int n_split_items, hipStream_t st) {
     CombineArgs c;
@@ -1221,6 +1218,9 @@ int run_stream(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int 
     return run_combine(h, a, BM, items, st);
 }
 
+// Launches the attention kernel for one kind and, if some items were split,
+// the combine kernel.  When `after_main` is given and a combine kernel
+// follows, the event is recorded between the two and *mid_recorded is set.
 int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len,
                   bool split_all, hipStream_t st, hipEvent_t after_main, bool *mid_recorded) {
     const int D = h->head_dim, H = h->heads;
