@@ -515,7 +515,7 @@ __device__ __forceinline__ void ring_barrier() {
 // same number of loads and the wait count stays exact -- then the scores
 // of t+1, the probabilities of t and P V of t, on this wave's NK keys of
 // each tile (starting koff bytes into it).
-template <int D, int NW, int NK, bool SW = true>
+template <int D, int NW, int NK>
 __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D, NW> &lo, const bf16x8 *qf,
                                           RowState<D> &st, int kv_begin, int ntiles, int koff, int key0,
                                           __amdgpu_buffer_rsrc_t none,
@@ -619,7 +619,7 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
     };
     auto step = [&](const f32x16 *s_cur, f32x16 *s_next, int t, const LDS_AS char *k_next,
                     const LDS_AS char *v_cur, LDS_AS char *k_fill, LDS_AS char *v_fill) {
-        if constexpr (SW && NK == BN && D == 128) {
+        if constexpr (NK == BN && D == 128) {
             step_sw(s_cur, s_next, t, k_next, v_cur, k_fill, v_fill);
         } else {
             ring_barrier<PER_TILE>();
@@ -641,7 +641,7 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
     f32x16 sA[NKB], sB[NKB];
     scores<D, NW, NK>(lo, qf, K0 + koff, sA);
     mask_tail<NK>(x, key0, sA);
-    if constexpr (SW && NK == BN && D == 128) update_max<D, NK>(x, sA, st);   // steps expect it settled
+    if constexpr (NK == BN && D == 128) update_max<D, NK>(x, sA, st);   // steps expect it settled
     int t = 0;
     for (; t + 4 <= ntiles; t += 4) {
         step(sA, sB, t, K1, V0, K3, V3);
@@ -1109,8 +1109,6 @@ int hip_fail(ltxattn_handle *h, hipError_t e) {
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// How many parts the v2a items are split into: enough workgroups to give
-// every CU two, at least four key tiles per part, at most NSPLIT_MAX.
 constexpr int LONG_ROWS = 1024;   // query and key rows from which 8-wave workgroups are used
 
 constexpr int RESIDENT_KV_MAX = 4 * BN;   // keys held in LDS by fa_kvres_kernel (128 KB)
@@ -1192,9 +1190,11 @@ int run_stream(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int 
     const int items = B * H * a.n_qtiles;
     a.groups = (items % 8 == 0 && h->num_cus % 8 == 0) ? 8 : 1;
     a.ipg = items / a.groups;
+    // Parts per item: one workgroup per CU, at most NSPLIT_MAX, at least
+    // four key tiles per part.
     int ns = h->num_cus / items;
     ns = ns < NSPLIT_MAX ? ns : NSPLIT_MAX;
-    const int by_len = kv_len / (4 * BN);   // parts of at least 4 tiles
+    const int by_len = kv_len / (4 * BN);
     ns = ns < by_len ? ns : by_len;
     ns = ns < 1 ? 1 : ns;
     a.split_len = ceil_div(ceil_div(kv_len, ns), BN) * BN;
