@@ -529,15 +529,18 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
         dma_tile<D, NW>(f ? x.kr : none, lo.k_src, (kv_begin + i * BN) * x.k_stride, kd, x.wave);
         dma_tile<D, NW>(f ? x.vr : none, lo.v_src, (kv_begin + i * BN) * x.v_stride, vd, x.wave);
     };
-    // Software-pipelined step (NK = BN = 64, D = 128): phase A interleaves
-    // the 16 score MFMAs of tile t+1, two per k-step, with the exponentials
-    // of tile t, four per k-step; phase B interleaves the 16 P V MFMAs of
-    // tile t with the row max of tile t+1, whose rescale decision closes the
-    // step.  Operand reads run two chunks ahead; the scheduling barriers
-    // keep this order.
+    // Software-pipelined step (D = 128; NK = 64, or 32 per key group): phase
+    // A interleaves the score MFMAs of tile t+1, NK/32 per k-step, with the
+    // exponentials of tile t, NK/16 per k-step; phase B interleaves the P V
+    // MFMAs of tile t, two per chunk, with the row max of tile t+1, whose
+    // rescale decision closes the step.  Operand reads run two chunks ahead;
+    // the scheduling barriers keep this order.
     auto step_sw = [&](const f32x16 *s_cur, f32x16 *s_next, int t, const LDS_AS char *k_next,
                        const LDS_AS char *v_cur, LDS_AS char *k_fill, LDS_AS char *v_fill) {
         constexpr int KS = D / 16, NDB = D / 32;
+        constexpr int EPC = NK / 2 / KS;            // exponentials per score chunk
+        static_assert(EPC == 4 || EPC == 2, "64 or 32 keys per wave and tile");
+        constexpr int MXC = 2 * NKB, MX0 = PS - NKB;  // P V chunks carrying the row max
         ring_barrier<PER_TILE>();
         load(t + 3, t + 3 < ntiles, k_fill, v_fill);
         bf16x8 pf[PS];
@@ -561,13 +564,19 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
             for (int kb = 0; kb < NKB; ++kb)
                 s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c % (LA + 1)][kb], qf[c],
                                                                      c == 0 ? f32x16{} : s_next[kb], 0, 0, 0);
-            {   // half (c & 1) of the exponentials of P k-step c / 2
+            if constexpr (EPC == 4) {   // half (c & 1) of the exponentials of P k-step c / 2
                 const int k = c >> 1, h = c & 1, kb = k >> 1, i = 2 * (k & 1) + h;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     pf[k][4 * h + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][i * 4 + j], x.c, -mc));
                 rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][4 * h], pf[k][4 * h + 1]}, one, rs0, false);
                 rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][4 * h + 2], pf[k][4 * h + 3]}, one, rs1, false);
+            } else {   // EPC == 2: exponentials 2c, 2c+1 (P k-step c / 4, row 2 (k % 2) + h, elements j, j+1)
+                const int n = 2 * c, k = n >> 3, h = (n >> 2) & 1, j = n & 3, kb = k >> 1, i = 2 * (k & 1) + h;
+                pf[k][4 * h + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][i * 4 + j], x.c, -mc));
+                pf[k][4 * h + j + 1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][i * 4 + j + 1], x.c, -mc));
+                if (c & 1) rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][4 * h + j], pf[k][4 * h + j + 1]}, one, rs1, false);
+                else rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][4 * h + j], pf[k][4 * h + j + 1]}, one, rs0, false);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -595,8 +604,8 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 st.o[2 * dbp + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[c % (LA + 1)][j], pf[k], st.o[2 * dbp + j], 0, 0, 0);
-            if (c >= 2 && c < 6) {   // a quarter of the row max of tile t+1
-                const int q4 = c - 2, kb = q4 >> 1, e0 = 8 * (q4 & 1);
+            if (c >= MX0 && c < MX0 + MXC) {   // 8 scores of the row max of tile t+1
+                const int q4 = c - MX0, kb = q4 >> 1, e0 = 8 * (q4 & 1);
 #pragma unroll
                 for (int e = e0; e < e0 + 8; e += 4) {
                     mx0 = fmaxf(fmaxf(mx0, s_next[kb][e]), s_next[kb][e + 1]);
@@ -619,7 +628,7 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
     };
     auto step = [&](const f32x16 *s_cur, f32x16 *s_next, int t, const LDS_AS char *k_next,
                     const LDS_AS char *v_cur, LDS_AS char *k_fill, LDS_AS char *v_fill) {
-        if constexpr (NK == BN && D == 128) {
+        if constexpr (D == 128) {
             step_sw(s_cur, s_next, t, k_next, v_cur, k_fill, v_fill);
         } else {
             ring_barrier<PER_TILE>();
@@ -641,7 +650,7 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
     f32x16 sA[NKB], sB[NKB];
     scores<D, NW, NK>(lo, qf, K0 + koff, sA);
     mask_tail<NK>(x, key0, sA);
-    if constexpr (NK == BN && D == 128) update_max<D, NK>(x, sA, st);   // steps expect it settled
+    if constexpr (D == 128) update_max<D, NK>(x, sA, st);   // steps expect it settled
     int t = 0;
     for (; t + 4 <= ntiles; t += 4) {
         step(sA, sB, t, K1, V0, K3, V3);
