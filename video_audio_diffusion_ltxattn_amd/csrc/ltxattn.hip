@@ -822,7 +822,7 @@ void fa_ring_kernel(const FaArgs a) {
 // ------------------------------------------------ resident short key streams
 // a2v and audio self-attention have at most a few hundred (audio) keys: a
 // workgroup loads all K/V tiles of its head into LDS once and then streams
-// a contiguous range of 128-query tiles past them.  The kernel is bound by
+// a contiguous range of query tiles (32 rows per wave) past them.  The kernel is bound by
 // reading Q and writing O, so both move as whole rows: each wave DMAs its 32
 // query rows into a wave-private LDS slot (1 KB = 4 rows per instruction),
 // takes its MFMA operands from there, and stages its output rows through
@@ -1235,9 +1235,9 @@ int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, i
     const int D = h->head_dim, H = h->heads;
     if (split_all) return run_stream(h, io, B, Sq, kv_len, st, after_main, mid_recorded);
     if (kv_len <= RESIDENT_KV_MAX) return run_resident_kv(h, io, B, Sq, kv_len, st);
-    // Long query and key streams (video self-attention) take 256-query
-    // workgroups: each K/V tile is then fetched once per 256 queries.  The
-    // others take 128 (more workgroups for the short, memory-bound ones).
+    // Long query and key streams (video self-attention) take the ring kernel
+    // with 256-query workgroups: each K/V tile is then fetched once per 256
+    // queries.  Other shapes take fa_fwd_kernel with 128.
     const int NW = (Sq >= LONG_ROWS && kv_len >= LONG_ROWS && D == 128) ? 8 : 4;
     const int BM = 32 * NW;
     FaArgs a;
