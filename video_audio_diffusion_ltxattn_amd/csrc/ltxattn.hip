@@ -826,19 +826,17 @@ void fa_ring_kernel(const FaArgs a) {
 // reading Q and writing O, so both move as whole rows: each wave DMAs its 32
 // query rows into a wave-private LDS slot (1 KB = 4 rows per instruction),
 // takes its MFMA operands from there, and stages its output rows through
-// the same slot for 16-byte-per-lane row stores.  With 4 waves per
-// workgroup each wave has two slots, so the next tile's Q streams in while
-// the current one is computed; with 8 waves (two per SIMD) each has one
-// slot and the next Q is fetched after the stores, the other wave of the
-// SIMD computing meanwhile.  No workgroup barrier is needed except when the
-// head changes.
+// the same slot for 16-byte-per-lane row stores; the next tile's Q is
+// fetched after the stores, the other wave of the SIMD computing meanwhile
+// (STAGED, 8 waves, D = 128).  Otherwise (more keys than leave room for the
+// slots, or D = 64) 4 waves take Q straight into registers, one tile ahead.
+// No workgroup barrier is needed except when the head changes.
 constexpr int KVRES_SLOT = 32 * 128 * 2;   // one wave's 32 rows of Q or O at D = 128 (8 KB)
 
 template <int D, int NW, bool STAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2)))
 void fa_kvres_kernel(const FaArgs a) {
     constexpr int BM = 32 * NW, KS = D / 16, NDB = D / 32, NKB = BN / 32, PS = BN / 16;
-    constexpr int NSLOT = NW == 4 ? 2 : 1;  // Q/O row slots per wave
     constexpr int TILE = BN * D * 2;
     constexpr int ROWB = D * 2;             // bytes per Q/O row
     extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];   // [kv tile][K, V] [wave][slot]
@@ -848,7 +846,7 @@ void fa_kvres_kernel(const FaArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hw = lane >> 5, l32 = lane & 31;
     const int nkt = (a.kv_len + BN - 1) / BN;
-    LDS_AS char *const slots = lds + nkt * 2 * TILE + wave * NSLOT * KVRES_SLOT;
+    LDS_AS char *const slot = lds + nkt * 2 * TILE + wave * KVRES_SLOT;   // STAGED: this wave's Q/O rows
 
     // This workgroup's items: a contiguous share of its group's range (the
     // group is its XCD's contiguous range of items, as in fa_fwd_kernel).
@@ -916,14 +914,12 @@ void fa_kvres_kernel(const FaArgs a) {
     };
 
     bf16x8 qf[KS], qn[KS];
-    if (STAGED) dma_q(i_begin, slots);
+    if (STAGED) dma_q(i_begin, slot);
     else regs_q(i_begin, qf);
     int cur_bh = -1;
     for (int item = i_begin; item < i_end; ++item) {
         const int qt = item % a.n_qtiles, bh = item / a.n_qtiles;
         const int b = bh / a.H, hh = bh % a.H;
-        LDS_AS char *const slot = slots + (NSLOT == 2 ? ((item - i_begin) & 1) * KVRES_SLOT : 0);
-        LDS_AS char *const next = slots + (NSLOT == 2 ? ((item - i_begin + 1) & 1) * KVRES_SLOT : 0);
         if (bh != cur_bh) {   // uniform: load every K/V tile of this head
             __syncthreads();  // all waves are done with the previous head's tiles
             x.kr = make_rsrc(a.k + b * a.k_sb + hh * a.k_sh, ((int64_t)(a.kv_len - 1) * a.k_ss + D) * 2);
@@ -936,14 +932,13 @@ void fa_kvres_kernel(const FaArgs a) {
             cur_bh = bh;
         }
         if (STAGED) {
-            // Q of this item is in `slot` (this wave's own DMA): wait for it,
-            // read the B operand, then start the next item's Q into `next`.
+            // Q of this item is in `slot` (this wave's own DMA): wait for it
+            // and read the B operand; the next item's Q follows the stores.
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
             for (int k = 0; k < KS; ++k)
                 qf[k] = __builtin_bit_cast(bf16x8,
                     *(const LDS_AS u32x4 *)(slot + l32 * ROWB + swz_k<D>(l32, 2 * k + hw) * 16));
-            if (NSLOT == 2 && item + 1 < i_end) dma_q(item + 1, next);
         } else if (item + 1 < i_end) {
             regs_q(item + 1, qn);
         }
@@ -987,7 +982,7 @@ void fa_kvres_kernel(const FaArgs a) {
                 const u32x4 w = *(const LDS_AS u32x4 *)(slot + r * ROWB + swz_k<D>(r, c) * 16);
                 if (qrow0 + r < a.Sq) *(u32x4 *)(obase + (int64_t)(qrow0 + r) * a.o_ss + c * 8) = w;
             }
-            if (NSLOT == 1 && item + 1 < i_end) {
+            if (item + 1 < i_end) {
                 // The slot's output rows have been read (the stores hold them); refill it.
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                 dma_q(item + 1, slot);
@@ -1140,8 +1135,7 @@ int run_resident_kv(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq,
     const int nkt = ceil_div(kv_len, BN);
     const size_t kv_lds = (size_t)nkt * 2 * BN * D * 2;
     // Row-staged Q/O: 8 waves x one 8 KB slot when the keys leave room for
-    // that, else 4 waves x two slots, else unstaged (operands straight from
-    // HBM into registers).
+    // that, else 4 unstaged waves (operands straight from HBM into registers).
     int nw = 4;
     bool staged = false;
     if (D == 128 && kv_lds + 8 * KVRES_SLOT <= LDS_BYTES) {
