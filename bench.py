@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cfg", type=int, default=3, help="workload (1..5); 3 is the headline block")
+    ap.add_argument("--overlap", action="store_true",
+                    help="ltxattn_block_attention_overlap: the audio-side kinds on a second stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -137,15 +139,16 @@ def main():
     stream = torch.cuda.current_stream()
     io = ba.make_io(dev, w.audio_kv_len, outs)
 
+    block = lt.ltxattn_block_attention_overlap if args.overlap else lt.ltxattn_block_attention
     for _ in range(args.warmup):
-        lt.ltxattn_block_attention(ba.handle, io, stream.cuda_stream)
+        block(ba.handle, io, stream.cuda_stream)
     torch.cuda.synchronize()
 
     lt.ltxattn_profile_begin(ba.handle, args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        lt.ltxattn_block_attention(ba.handle, io, stream.cuda_stream)
+        block(ba.handle, io, stream.cuda_stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     rec = lt.ltxattn_profile_read(ba.handle, args.steps)
@@ -188,7 +191,8 @@ def main():
         "config": {"workload": f"LTX-2 block attention set, {w.name}",
                    "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "video_tokens": w.video_len, "audio_tokens": w.audio_kv_len,
-                   "audio_buffer_rows": w.audio_len, "parallelism": "none (1 GPU)"},
+                   "audio_buffer_rows": w.audio_len, "parallelism": "none (1 GPU)",
+                 "schedule": "overlap" if args.overlap else "sequential"},
         "kinds": kinds,
         "roofline": {"kernel": "fa_ring_kernel<128, 8, 1> (video self-attention)",
                      "bound": "mfma", "achieved": round(achieved, 2),

@@ -131,6 +131,22 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out);
  * Errors: INVALID_ARG, UNSUPPORTED (checked before any launch), HIP. */
 int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void *hip_stream);
 
+/* The same block call with the audio side running beside video
+ * self-attention: VIDEO_SELF is enqueued on hip_stream, V2A, A2V and
+ * AUDIO_SELF (same order) on a stream the handle owns, which is forked from
+ * hip_stream at the start of the call and joined back into it at the end
+ * (HIP events; no host synchronisation).  Work enqueued on hip_stream after
+ * the call therefore sees all four outputs, and the call can be captured
+ * into a HIP graph from hip_stream.  Outputs are bit-identical to
+ * ltxattn_block_attention's (the same kernels; the two sides use separate
+ * workspace regions).  Calls on one handle must not overlap each other,
+ * as for ltxattn_block_attention.  The audio side is a few percent of a
+ * block (PR #16228, "Description"); whether running it beside video
+ * self-attention shortens the block depends on how much of the device the
+ * video kernel leaves free.
+ * Errors: as ltxattn_block_attention. */
+int ltxattn_block_attention_overlap(ltxattn_handle *h, const ltxattn_block_io *io, void *hip_stream);
+
 /* Validate a block call against a configuration without touching any
  * device: returns exactly the status ltxattn_block_attention would return
  * from its argument checks (LTXATTN_OK if the call would be launched).
@@ -150,10 +166,11 @@ const char *ltxattn_status_string(int status);
  * the calling thread.  0 if none. */
 int ltxattn_last_hip_error(const ltxattn_handle *h);
 
-/* Per-kind timing with HIP events recorded on the call's stream.
+/* Per-kind timing with HIP events recorded on the stream each kind runs on.
  * ltxattn_profile_begin creates events for up to max_calls block calls
- * (created here, outside any timed region); each later block call records
- * events around every kind and one after each kind's attention kernel.
+ * (created here, outside any timed region); each later block call (either
+ * entry point) records events around the call, around every kind and one
+ * after each kind's attention kernel when a combine kernel follows.
  * ltxattn_profile_read waits for the recorded events and writes
  * LTXATTN_PROFILE_FLOATS floats per recorded call c < *n_calls (at most
  * max_calls), in milliseconds:

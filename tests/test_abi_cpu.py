@@ -58,6 +58,7 @@ def test_create_rejects_before_device():
 def test_null_handles():
     io = lt.ltxattn_block_io()
     assert lt._lib.ltxattn_block_attention(None, ctypes.byref(io), None) == lt.LTXATTN_ERR_INVALID_ARG
+    assert lt._lib.ltxattn_block_attention_overlap(None, ctypes.byref(io), None) == lt.LTXATTN_ERR_INVALID_ARG
     assert lt._lib.ltxattn_destroy(None) == lt.LTXATTN_OK
     assert lt._lib.ltxattn_profile_begin(None, 4) == lt.LTXATTN_ERR_INVALID_ARG
     assert lt._lib.ltxattn_last_hip_error(None) == 0

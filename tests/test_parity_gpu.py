@@ -260,3 +260,53 @@ def test_create_on_missing_device(lt, torch):
     with pytest.raises(lt.LtxattnError) as e:
         lt.ltxattn_create(cfg)
     assert e.value.status == lt.LTXATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 17])
+def test_overlap_matches_sequential(lt, torch, cfg):
+    """ltxattn_block_attention_overlap runs the audio side on the handle's
+    second stream; the kernels are the same, so every output must equal the
+    sequential call's bit for bit."""
+    w = RAGGED[[r.cfg for r in RAGGED].index(cfg)] if cfg > 10 else synth.WORKLOADS[cfg]
+    inputs = synth.make_block_inputs(w)
+    dev = {n: to_device(a) for n, a in inputs.items()}
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
+    log(f"  overlap vs sequential: {w.name}")
+    seq = ba(dev, w.audio_kv_len)
+    ovl = ba(dev, w.audio_kv_len, overlap=True)
+    torch.cuda.synchronize()
+    for k in KINDS:
+        assert torch.equal(seq[k].view(torch.int16), ovl[k].view(torch.int16)), k
+    ba.close()
+
+
+@pytest.mark.parametrize("overlap", [False, True])
+def test_graph_capture_replays(lt, torch, overlap):
+    """The block call captured into a HIP graph from the caller's stream
+    (with overlap, the side stream joins the capture through the fork event)
+    and replayed three times, with eager work and synchronisation between
+    the replays: every replay equals the eager result bit for bit."""
+    w = RAGGED[[r.cfg for r in RAGGED].index(17)]
+    inputs = synth.make_block_inputs(w)
+    dev = {n: to_device(a) for n, a in inputs.items()}
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
+    want = ba(dev, w.audio_kv_len, overlap=overlap)
+    torch.cuda.synchronize()
+    outs = {k: torch.empty_like(v) for k, v in want.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    log(f"  graph capture, overlap={overlap}")
+    with torch.cuda.graph(g, stream=s):
+        ba(dev, w.audio_kv_len, outs=outs, stream=s, overlap=overlap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs.values():
+            o.zero_()                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in KINDS:
+            assert torch.equal(outs[k].view(torch.int16), want[k].view(torch.int16)), (rep, k)
+    del g
+    ba.close()

@@ -82,7 +82,7 @@ constexpr int BM_MAX = 256;      // most query rows per workgroup (8 waves x 32)
 constexpr int WAVES_PER_CU = 8;  // 2 per SIMD: the register budget of the attention kernel
 constexpr int NSPLIT_MAX = 16;   // key-range parts of a split work item
 constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
-constexpr int PROF_EVENTS = 9;          // events per profiled block call
+constexpr int PROF_EVENTS = 14;         // per profiled block call: start, end, 3 per kind
 
 struct FaArgs {
     const __bf16 *q, *k, *v;
@@ -1075,9 +1075,16 @@ struct ltxattn_handle {
     int device;
     int heads, head_dim, max_batch, max_video_len, max_audio_len;
     int num_cus;
-    float *ws_o;
-    float *ws_ml;
-    int64_t ws_rows;
+    // Workspace of split items, two regions so that v2a can run beside the
+    // other kinds: rows [0, tail_rows) for the split last round of a
+    // self-attention, rows [tail_rows, tail_rows + v2a_rows) for v2a.
+    float *ws_o;      // [rows][head_dim]
+    float *ws_ml;     // [rows][2]
+    int64_t tail_rows, v2a_rows;
+    // ltxattn_block_attention_overlap: the stream the audio-side kinds run
+    // on, and the events that fork it from and join it to the caller's.
+    hipStream_t side;
+    hipEvent_t fork, join;
     int last_hip_error;
     // profiling
     hipEvent_t *events;
@@ -1161,7 +1168,7 @@ int run_resident_kv(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq,
 // Merge the key-range parts of n_split_items items (fa_combine_kernel).
 int run_combine(ltxattn_handle *h, const FaArgs &a, int bm, int n_split_items, hipStream_t st) {
     CombineArgs c;
-    c.part_o = h->ws_o; c.part_ml = h->ws_ml;
+    c.part_o = a.part_o; c.part_ml = a.part_ml;
     c.o = a.o; c.o_sb = a.o_sb; c.o_ss = a.o_ss; c.o_sh = a.o_sh;
     c.H = a.H; c.Sq = a.Sq; c.bm = bm; c.n_qtiles = a.n_qtiles; c.ipg = a.ipg; c.wpg = a.wpg;
     c.n_split_items = n_split_items; c.nsplit = a.nsplit;
@@ -1204,10 +1211,10 @@ int run_stream(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int 
     ns = ceil_div(kv_len, a.split_len);    // every part holds at least one key
     a.nsplit = ns;
     a.wpg = ns == 1 ? a.ipg : 0;           // one part: every item is whole
-    a.part_o = h->ws_o;
-    a.part_ml = h->ws_ml;
+    a.part_o = h->ws_o + h->tail_rows * D;  // the v2a region of the workspace
+    a.part_ml = h->ws_ml + h->tail_rows * 2;
     a.total = items * ns;
-    if (ns > 1 && (int64_t)items * ns * BM > h->ws_rows) return LTXATTN_ERR_INVALID_ARG;  // cannot happen
+    if (ns > 1 && (int64_t)items * ns * BM > h->v2a_rows) return LTXATTN_ERR_INVALID_ARG;  // cannot happen
     const size_t lds = (size_t)RING_STAGES * 2 * BN * D * 2;
     if (D == 128) hipLaunchKernelGGL((fa_ring_kernel<128, RING_NW, 2>), dim3(a.total), dim3(64 * RING_NW), lds, st, a);
     else hipLaunchKernelGGL((fa_ring_kernel<64, RING_NW, 2>), dim3(a.total), dim3(64 * RING_NW), lds, st, a);
@@ -1271,11 +1278,11 @@ int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, i
     a.groups = groups;
     a.ipg = ipg;
     a.wpg = ipg - spg;
-    a.part_o = h->ws_o;
+    a.part_o = h->ws_o;                    // the tail region of the workspace
     a.part_ml = h->ws_ml;
     a.total = groups * (a.wpg + spg * ns);
     const int n_split_items = groups * spg;
-    if ((int64_t)n_split_items * ns * BM > h->ws_rows) return LTXATTN_ERR_INVALID_ARG;  // cannot happen
+    if ((int64_t)n_split_items * ns * BM > h->tail_rows) return LTXATTN_ERR_INVALID_ARG;  // cannot happen
 
     if (D == 128 && NW == 8)
         hipLaunchKernelGGL((fa_ring_kernel<128, RING_NW, 1>), dim3(a.total), dim3(64 * RING_NW),
@@ -1332,6 +1339,75 @@ int validate_block(const ltxattn_config &caps, const ltxattn_block_io *io, bool 
         }
     }
     return LTXATTN_OK;
+}
+
+// The block call.  Kinds run in KIND_ORDER on the caller's stream; with
+// `overlap`, the audio-side kinds (v2a, a2v, audio self) run on the
+// handle's side stream instead, forked from the caller's stream at the
+// start of the call and joined back into it at the end, so the call stays
+// one ordered unit on the caller's stream (and can be captured into a HIP
+// graph from it).  Profiling events, if on: 0 and 1 open and close the call
+// on the caller's stream; 2 + 3k, 3 + 3k, 4 + 3k are the start of kind k,
+// the end of its attention kernel when a combine kernel follows, and its
+// end, on the stream that runs it.
+int enqueue_block(ltxattn_handle *h, const ltxattn_block_io *io, hipStream_t st, bool overlap) {
+    if (!h || !io) return LTXATTN_ERR_INVALID_ARG;
+    const ltxattn_config caps = {h->device, h->heads, h->head_dim, h->max_batch, h->max_video_len,
+                                 h->max_audio_len};
+    bool on[4];
+    const int vrc = validate_block(caps, io, on);
+    if (vrc) return vrc;
+    const int B = io->batch, Sv = io->video_len, La = io->audio_len, Lk = io->audio_kv_len;
+    const int q_rows[4] = {Sv, La, Sv, La};
+
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return hip_fail(h, g.err);
+    hipEvent_t *ev = nullptr;
+    bool *mid = nullptr;
+    if (h->events && h->prof_n < h->prof_max) {
+        ev = h->events + (int64_t)h->prof_n * PROF_EVENTS;
+        mid = h->prof_mid + (int64_t)h->prof_n * 4;
+        for (int n = 0; n < 4; ++n) mid[n] = false;
+        ++h->prof_n;
+    }
+    hipError_t e;
+    if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail(h, e);
+    if (overlap) {
+        if ((e = hipEventRecord(h->fork, st)) != hipSuccess) return hip_fail(h, e);
+        if ((e = hipStreamWaitEvent(h->side, h->fork, 0)) != hipSuccess) return hip_fail(h, e);
+    }
+    for (int n = 0; n < 4; ++n) {
+        const int k = KIND_ORDER[n];
+        hipStream_t ks = (overlap && k != LTXATTN_VIDEO_SELF) ? h->side : st;
+        if (ev && (e = hipEventRecord(ev[2 + 3 * k], ks)) != hipSuccess) return hip_fail(h, e);
+        if (on[k]) {
+            const int kv_len = (k == LTXATTN_AUDIO_SELF || k == LTXATTN_A2V) ? Lk : Sv;
+            const int rc = run_attention(h, io->attn[k], B, q_rows[k], kv_len, k == LTXATTN_V2A, ks,
+                                         ev ? ev[3 + 3 * k] : nullptr, mid ? &mid[k] : nullptr);
+            if (rc) return rc;
+        }
+        if (ev && (e = hipEventRecord(ev[4 + 3 * k], ks)) != hipSuccess) return hip_fail(h, e);
+    }
+    if (overlap) {
+        if ((e = hipEventRecord(h->join, h->side)) != hipSuccess) return hip_fail(h, e);
+        if ((e = hipStreamWaitEvent(st, h->join, 0)) != hipSuccess) return hip_fail(h, e);
+    }
+    if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return hip_fail(h, e);
+    return LTXATTN_OK;
+}
+
+// Frees what create allocated (null members are skipped) and the handle;
+// returns the first error.
+hipError_t release(ltxattn_handle *h) {
+    hipError_t first = hipSuccess;
+    auto keep = [&](hipError_t e) { if (first == hipSuccess && e != hipSuccess) first = e; };
+    if (h->join) keep(hipEventDestroy(h->join));
+    if (h->fork) keep(hipEventDestroy(h->fork));
+    if (h->side) keep(hipStreamDestroy(h->side));
+    if (h->ws_ml) keep(hipFree(h->ws_ml));
+    if (h->ws_o) keep(hipFree(h->ws_o));
+    free(h);
+    return first;
 }
 
 }  // namespace
@@ -1395,21 +1471,24 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
         e = hipFuncSetAttribute((const void *)&fa_ring_kernel<128, RING_NW, 1>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 128 * 2);
     if (e != hipSuccess) { g_create_hip_error = (int)e; free(h); return LTXATTN_ERR_HIP; }
-    // Workspace of the split items, BM rows per part: v2a splits every audio
-    // query tile of every (batch, head) into at most NSPLIT_MAX parts; the
-    // tail split of the other kinds uses at most one round of workgroups.
-    const int64_t v2a_rows = (int64_t)h->max_batch * h->heads * ceil_div(h->max_audio_len, 128) * NSPLIT_MAX * 128;
-    const int64_t tail_rows = (int64_t)WAVES_PER_CU / 4 * h->num_cus * BM_MAX;
-    h->ws_rows = v2a_rows > tail_rows ? v2a_rows : tail_rows;
-    e = hipMalloc((void **)&h->ws_o, (size_t)h->ws_rows * h->head_dim * sizeof(float));
-    if (e != hipSuccess) { g_create_hip_error = (int)e; (void)hipGetLastError(); free(h); return LTXATTN_ERR_OOM; }
-    e = hipMalloc((void **)&h->ws_ml, (size_t)h->ws_rows * 2 * sizeof(float));
+    // Workspace of the split items, BM rows per part: the tail split of a
+    // self-attention uses at most one round of workgroups; v2a splits every
+    // audio query tile of every (batch, head) into at most NSPLIT_MAX parts.
+    h->tail_rows = (int64_t)WAVES_PER_CU / 4 * h->num_cus * BM_MAX;
+    h->v2a_rows = (int64_t)h->max_batch * h->heads * ceil_div(h->max_audio_len, 128) * NSPLIT_MAX * 128;
+    const int64_t rows = h->tail_rows + h->v2a_rows;
+    int status = LTXATTN_OK;
+    e = hipMalloc((void **)&h->ws_o, (size_t)rows * h->head_dim * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void **)&h->ws_ml, (size_t)rows * 2 * sizeof(float));
+    if (e != hipSuccess) status = LTXATTN_ERR_OOM;
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
     if (e != hipSuccess) {
         g_create_hip_error = (int)e;
         (void)hipGetLastError();
-        (void)hipFree(h->ws_o);
-        free(h);
-        return LTXATTN_ERR_OOM;
+        release(h);
+        return status ? status : LTXATTN_ERR_HIP;
     }
     *out = h;
     return LTXATTN_OK;
@@ -1419,10 +1498,7 @@ int ltxattn_destroy(ltxattn_handle *h) {
     if (!h) return LTXATTN_OK;
     DeviceGuard g(h->device);
     if (h->events) ltxattn_profile_end(h);
-    hipError_t e1 = hipFree(h->ws_o);
-    hipError_t e2 = hipFree(h->ws_ml);
-    free(h);
-    return (e1 == hipSuccess && e2 == hipSuccess) ? LTXATTN_OK : LTXATTN_ERR_HIP;
+    return release(h) == hipSuccess ? LTXATTN_OK : LTXATTN_ERR_HIP;
 }
 
 int ltxattn_last_hip_error(const ltxattn_handle *h) { return h ? h->last_hip_error : g_create_hip_error; }
@@ -1436,43 +1512,11 @@ int ltxattn_check_block(const ltxattn_config *cfg, const ltxattn_block_io *io) {
 }
 
 int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void *hip_stream) {
-    if (!h || !io) return LTXATTN_ERR_INVALID_ARG;
-    const ltxattn_config caps = {h->device, h->heads, h->head_dim, h->max_batch, h->max_video_len,
-                                 h->max_audio_len};
-    bool on[4];
-    const int vrc = validate_block(caps, io, on);
-    if (vrc) return vrc;
-    const int B = io->batch, Sv = io->video_len, La = io->audio_len, Lk = io->audio_kv_len;
-    const int q_rows[4] = {Sv, La, Sv, La};
+    return enqueue_block(h, io, (hipStream_t)hip_stream, false);
+}
 
-    DeviceGuard g(h->device);
-    if (g.err != hipSuccess) return hip_fail(h, g.err);
-    hipStream_t st = (hipStream_t)hip_stream;
-    hipEvent_t *ev = nullptr;
-    bool *mid = nullptr;
-    if (h->events && h->prof_n < h->prof_max) {
-        ev = h->events + (int64_t)h->prof_n * PROF_EVENTS;
-        mid = h->prof_mid + (int64_t)h->prof_n * 4;
-        for (int n = 0; n < 4; ++n) mid[n] = false;
-        ++h->prof_n;
-    }
-    hipError_t e;
-    if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail(h, e);
-
-    // Kinds run in KIND_ORDER.  For the n-th kind in that order, event
-    // 2 + 2n closes the kind, and event 1 + 2n separates its attention
-    // kernel from a combine kernel if one follows.
-    for (int n = 0; n < 4; ++n) {
-        const int k = KIND_ORDER[n];
-        if (on[k]) {
-            const int kv_len = (k == LTXATTN_AUDIO_SELF || k == LTXATTN_A2V) ? Lk : Sv;
-            const int rc = run_attention(h, io->attn[k], B, q_rows[k], kv_len, k == LTXATTN_V2A, st,
-                                         ev ? ev[1 + 2 * n] : nullptr, mid ? &mid[n] : nullptr);
-            if (rc) return rc;
-        }
-        if (ev && (e = hipEventRecord(ev[2 + 2 * n], st)) != hipSuccess) return hip_fail(h, e);
-    }
-    return LTXATTN_OK;
+int ltxattn_block_attention_overlap(ltxattn_handle *h, const ltxattn_block_io *io, void *hip_stream) {
+    return enqueue_block(h, io, (hipStream_t)hip_stream, true);
 }
 
 int ltxattn_profile_begin(ltxattn_handle *h, int32_t max_calls) {
@@ -1512,20 +1556,20 @@ int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_
     const int n = h->prof_n < max_calls ? h->prof_n : max_calls;
     for (int c = 0; c < n; ++c) {
         hipEvent_t *ev = h->events + (int64_t)c * PROF_EVENTS;
-        hipError_t e = hipEventSynchronize(ev[PROF_EVENTS - 1]);
+        hipError_t e = hipEventSynchronize(ev[1]);   // the call's end: after every kind
         if (e != hipSuccess) return hip_fail(h, e);
         float *out = ms + (int64_t)c * LTXATTN_PROFILE_FLOATS;
-        for (int s = 0; s < 4; ++s) {
+        for (int k = 0; k < 4; ++k) {
             float tot = 0.f, ker = 0.f;
-            if ((e = hipEventElapsedTime(&tot, ev[2 * s], ev[2 * s + 2])) != hipSuccess) return hip_fail(h, e);
-            const bool m = h->prof_mid[(int64_t)c * 4 + s];
-            if ((e = hipEventElapsedTime(&ker, ev[2 * s], ev[m ? 2 * s + 1 : 2 * s + 2])) != hipSuccess)
+            if ((e = hipEventElapsedTime(&tot, ev[2 + 3 * k], ev[4 + 3 * k])) != hipSuccess) return hip_fail(h, e);
+            const bool m = h->prof_mid[(int64_t)c * 4 + k];
+            if ((e = hipEventElapsedTime(&ker, ev[2 + 3 * k], ev[m ? 3 + 3 * k : 4 + 3 * k])) != hipSuccess)
                 return hip_fail(h, e);
-            out[KIND_ORDER[s]] = tot;
-            out[5 + KIND_ORDER[s]] = ker;
+            out[k] = tot;
+            out[5 + k] = ker;
         }
         float tot = 0.f;
-        if ((e = hipEventElapsedTime(&tot, ev[0], ev[PROF_EVENTS - 1])) != hipSuccess) return hip_fail(h, e);
+        if ((e = hipEventElapsedTime(&tot, ev[0], ev[1])) != hipSuccess) return hip_fail(h, e);
         out[4] = tot;
     }
     *n_calls = n;

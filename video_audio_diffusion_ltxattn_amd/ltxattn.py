@@ -80,6 +80,7 @@ def _load():
     sig = {
         "ltxattn_create": ([ctypes.POINTER(ltxattn_config), ctypes.POINTER(P)], ctypes.c_int),
         "ltxattn_block_attention": ([P, ctypes.POINTER(ltxattn_block_io), P], ctypes.c_int),
+        "ltxattn_block_attention_overlap": ([P, ctypes.POINTER(ltxattn_block_io), P], ctypes.c_int),
         "ltxattn_check_block": ([ctypes.POINTER(ltxattn_config), ctypes.POINTER(ltxattn_block_io)],
                                 ctypes.c_int),
         "ltxattn_destroy": ([P], ctypes.c_int),
@@ -98,7 +99,8 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("ltxattn_create", "ltxattn_block_attention", "ltxattn_check_block",
+EXPORTED = ("ltxattn_create", "ltxattn_block_attention", "ltxattn_block_attention_overlap",
+            "ltxattn_check_block",
             "ltxattn_destroy", "ltxattn_status_string", "ltxattn_last_hip_error",
             "ltxattn_profile_begin", "ltxattn_profile_read", "ltxattn_profile_end")
 
@@ -120,6 +122,13 @@ def ltxattn_block_attention(h, io: ltxattn_block_io, stream: int) -> None:
     rc = _lib.ltxattn_block_attention(h, ctypes.byref(io), ctypes.c_void_p(stream))
     if rc != LTXATTN_OK:
         raise LtxattnError(rc, "ltxattn_block_attention",
+                           _lib.ltxattn_last_hip_error(h) if rc == LTXATTN_ERR_HIP else 0)
+
+
+def ltxattn_block_attention_overlap(h, io: ltxattn_block_io, stream: int) -> None:
+    rc = _lib.ltxattn_block_attention_overlap(h, ctypes.byref(io), ctypes.c_void_p(stream))
+    if rc != LTXATTN_OK:
+        raise LtxattnError(rc, "ltxattn_block_attention_overlap",
                            _lib.ltxattn_last_hip_error(h) if rc == LTXATTN_ERR_HIP else 0)
 
 
@@ -221,12 +230,13 @@ class BlockAttention:
         return io
 
     def __call__(self, streams: dict, audio_kv_len: int, kinds=KIND_NAMES, outs: dict = None,
-                 stream=None) -> dict:
+                 stream=None, overlap: bool = False) -> dict:
         import torch
         if outs is None:
             vq, aq = streams["video_q"], streams["audio_q"]
             outs = {k: torch.empty_like(vq if k in ("video_self", "a2v") else aq) for k in kinds}
         io = self.make_io(streams, audio_kv_len, outs)
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
-        ltxattn_block_attention(self.handle, io, s.cuda_stream)
+        call = ltxattn_block_attention_overlap if overlap else ltxattn_block_attention
+        call(self.handle, io, s.cuda_stream)
         return outs
