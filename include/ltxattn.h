@@ -74,8 +74,8 @@ typedef struct ltxattn_handle ltxattn_handle;
 /* Fixed at create time.  heads and head_dim are shared by all four
  * attentions.  The max_* capacities bound every later call and size the
  * device workspace of split work items (the key-range parts of v2a and of
- * an incomplete last round of video self-attention; about 68 MB at 32 heads
- * of 128). */
+ * an incomplete last round of video self-attention, in separate regions;
+ * about 100 MB at 32 heads of 128 on a 256-CU device). */
 typedef struct {
     int32_t device;        /* HIP device ordinal the handle and its kernels use */
     int32_t heads;         /* H >= 1 */
