@@ -239,19 +239,27 @@ def test_kinds_are_independent(lt, torch):
         assert np.array_equal(one[k], full[k]), k
 
 
-def test_profile_events(lt, torch):
-    w = synth.WORKLOADS[1]
+@pytest.mark.parametrize("overlap", [False, True])
+def test_profile_events(lt, torch, overlap):
+    w = RAGGED[[r.cfg for r in RAGGED].index(17)]
     dev = {n: to_device(a) for n, a in synth.make_block_inputs(w).items()}
     ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
     lt.ltxattn_profile_begin(ba.handle, 4)
     for _ in range(2):
-        ba(dev, w.audio_kv_len)
+        ba(dev, w.audio_kv_len, overlap=overlap)
     rec = lt.ltxattn_profile_read(ba.handle, 4)
     lt.ltxattn_profile_end(ba.handle)
     assert len(rec) == 2
     for r in rec:
-        assert r["total"] > 0 and r["video_self"] > 0
-        assert r["total"] + 1e-3 >= sum(r[k] for k in KINDS)
+        assert all(r[k] > 0 for k in KINDS)
+        for k in KINDS:   # the attention kernel alone is part of its kind
+            assert 0 < r["kernel"][k] <= r[k] + 1e-3
+            assert r[k] <= r["total"] + 1e-3
+        if not overlap:   # one stream: the kinds add up within the call
+            assert r["total"] + 1e-3 >= sum(r[k] for k in KINDS)
+        else:             # two streams: the call lasts at least its longer side
+            side = r["v2a"] + r["a2v"] + r["audio_self"]
+            assert r["total"] + 1e-3 >= max(r["video_self"], side)
     ba.close()
 
 
