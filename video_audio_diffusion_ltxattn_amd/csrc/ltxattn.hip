@@ -175,6 +175,9 @@ __device__ __forceinline__ void tile_barrier() {
 // are taken against the stale max and stay below 2^RESCALE_LOG2.  Exact
 // algebra: O / l does not depend on which max was subtracted.
 constexpr float RESCALE_LOG2 = 8.0f;
+// The same bound on a lane's sum of probabilities in one tile: a sum at most
+// 2^RESCALE_LOG2 has every term at most 2^RESCALE_LOG2.
+constexpr float RESCALE_SUM = 256.0f;
 
 template <int D>
 struct RowState {
@@ -529,26 +532,25 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
         dma_tile<D, NW>(f ? x.kr : none, lo.k_src, (kv_begin + i * BN) * x.k_stride, kd, x.wave);
         dma_tile<D, NW>(f ? x.vr : none, lo.v_src, (kv_begin + i * BN) * x.v_stride, vd, x.wave);
     };
-    // Software-pipelined step (D = 128; NK = 64, or 32 per key group): phase
-    // A interleaves the score MFMAs of tile t+1, NK/32 per k-step, with the
-    // exponentials of tile t, NK/16 per k-step; phase B interleaves the P V
-    // MFMAs of tile t, two per chunk, with the row max of tile t+1, whose
-    // rescale decision closes the step.  Operand reads run two chunks ahead;
-    // the scheduling barriers keep this order.
+    // The step at D = 128 (NK = 64, or 32 per key group), in three blocks:
+    // the score MFMAs of tile t+1; the probabilities of tile t and their row
+    // sums; the P V MFMAs of tile t.  Operand reads run LA k-steps ahead of
+    // their MFMAs and scheduling barriers hold that order.  Every wave starts
+    // the step at the same barrier; the two waves of a SIMD drift apart
+    // within it, so one's MFMA blocks cover part of the other's exponentials.
+    // Probabilities are taken against the max in use without computing the
+    // tile's max first: if no lane's sum of its 2^(s c - m c) exceeds
+    // RESCALE_SUM, none of them does either, which is the bound the lazy
+    // rescale keeps; otherwise (the first tiles, or a new max) the wave takes
+    // the tile's max, rescales and computes the probabilities again.
     auto step_sw = [&](const f32x16 *s_cur, f32x16 *s_next, int t, const LDS_AS char *k_next,
                        const LDS_AS char *v_cur, LDS_AS char *k_fill, LDS_AS char *v_fill) {
         constexpr int KS = D / 16, NDB = D / 32;
-        constexpr int EPC = NK / 2 / KS;            // exponentials per score chunk
-        static_assert(EPC == 4 || EPC == 2, "64 or 32 keys per wave and tile");
-        constexpr int MXC = 2 * NKB, MX0 = PS - NKB;  // P V chunks carrying the row max
+        constexpr int LA = 2;
         ring_barrier<PER_TILE>();
         load(t + 3, t + 3 < ntiles, k_fill, v_fill);
-        bf16x8 pf[PS];
-        constexpr int LA = 2;   // operand reads run LA chunks ahead of their MFMAs
+
         bf16x8 kop[LA + 1][NKB];
-        float rs0 = 0.f, rs1 = 0.f;
-        const float mc = st.m * x.c;
-        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
         auto read_k = [&](int k, bf16x8 *op) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
@@ -564,24 +566,52 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
             for (int kb = 0; kb < NKB; ++kb)
                 s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c % (LA + 1)][kb], qf[c],
                                                                      c == 0 ? f32x16{} : s_next[kb], 0, 0, 0);
-            if constexpr (EPC == 4) {   // half (c & 1) of the exponentials of P k-step c / 2
-                const int k = c >> 1, h = c & 1, kb = k >> 1, i = 2 * (k & 1) + h;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    pf[k][4 * h + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][i * 4 + j], x.c, -mc));
-                rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][4 * h], pf[k][4 * h + 1]}, one, rs0, false);
-                rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][4 * h + 2], pf[k][4 * h + 3]}, one, rs1, false);
-            } else {   // EPC == 2: exponentials 2c, 2c+1 (P k-step c / 4, row 2 (k % 2) + h, elements j, j+1)
-                const int n = 2 * c, k = n >> 3, h = (n >> 2) & 1, j = n & 3, kb = k >> 1, i = 2 * (k & 1) + h;
-                pf[k][4 * h + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][i * 4 + j], x.c, -mc));
-                pf[k][4 * h + j + 1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][i * 4 + j + 1], x.c, -mc));
-                if (c & 1) rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][4 * h + j], pf[k][4 * h + j + 1]}, one, rs1, false);
-                else rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][4 * h + j], pf[k][4 * h + j + 1]}, one, rs0, false);
-            }
             __builtin_amdgcn_sched_barrier(0);
         }
-        st.l += rs0 + rs1;
         mask_tail<NK>(x, key0 + (t + 1) * BN, s_next);
+
+        // pf[k][4h + j] = 2^(s c - m c) of score s_cur[k / 2][4 (2 (k % 2) + h) + j]
+        // (the B-operand order of P V k-step k), row sums in two chains.
+        bf16x8 pf[PS];
+        auto probs_sum = [&]() {
+            const float mc = st.m * x.c;
+            const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+            float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+            for (int k = 0; k < PS; ++k)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int kb = k >> 1, i = 2 * (k & 1) + h;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pf[k][4 * h + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[kb][i * 4 + j], x.c, -mc));
+                    rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][4 * h], pf[k][4 * h + 1]}, one, rs0, false);
+                    rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][4 * h + 2], pf[k][4 * h + 3]}, one, rs1, false);
+                }
+            return rs0 + rs1;
+        };
+        float rsum = probs_sum();
+        if (__builtin_amdgcn_ballot_w64(!(rsum <= RESCALE_SUM))) {
+            float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; e += 4) {
+                    mx0 = fmaxf(fmaxf(mx0, s_cur[kb][e]), s_cur[kb][e + 1]);
+                    mx1 = fmaxf(fmaxf(mx1, s_cur[kb][e + 2]), s_cur[kb][e + 3]);
+                }
+            const float m_new = fmaxf(st.m, xhalf_max(fmaxf(mx0, mx1)));
+            const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * x.c);
+            st.m = m_new;
+            st.l *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
+            rsum = probs_sum();
+        }
+        st.l += rsum;
+
         bf16x8 vop[LA + 1][2];
         auto read_v = [&](int c, bf16x8 *op) {
             const int k = c >> 1, dbp = c & 1;
@@ -593,7 +623,6 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
                 op[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
             }
         };
-        float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
         for (int c = 0; c < LA; ++c) read_v(c, vop[c]);
         __builtin_amdgcn_sched_barrier(0);
@@ -604,26 +633,7 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 st.o[2 * dbp + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[c % (LA + 1)][j], pf[k], st.o[2 * dbp + j], 0, 0, 0);
-            if (c >= MX0 && c < MX0 + MXC) {   // 8 scores of the row max of tile t+1
-                const int q4 = c - MX0, kb = q4 >> 1, e0 = 8 * (q4 & 1);
-#pragma unroll
-                for (int e = e0; e < e0 + 8; e += 4) {
-                    mx0 = fmaxf(fmaxf(mx0, s_next[kb][e]), s_next[kb][e + 1]);
-                    mx1 = fmaxf(fmaxf(mx1, s_next[kb][e + 2]), s_next[kb][e + 3]);
-                }
-            }
             __builtin_amdgcn_sched_barrier(0);
-        }
-        const float m_t = xhalf_max(fmaxf(mx0, mx1));
-        if (__builtin_amdgcn_ballot_w64((m_t - st.m) * x.c > RESCALE_LOG2)) {
-            const float m_new = fmaxf(st.m, m_t);
-            const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * x.c);
-            st.m = m_new;
-            st.l *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
         }
     };
     auto step = [&](const f32x16 *s_cur, f32x16 *s_next, int t, const LDS_AS char *k_next,
@@ -1487,7 +1497,7 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
     if (e != hipSuccess) {
         g_create_hip_error = (int)e;
         (void)hipGetLastError();
-        release(h);
+        (void)release(h);   // the failure above is the one reported
         return status ? status : LTXATTN_ERR_HIP;
     }
     *out = h;
