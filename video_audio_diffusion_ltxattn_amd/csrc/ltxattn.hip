@@ -517,9 +517,17 @@ __device__ __forceinline__ void ring_barrier() {
 // zero-sized resource past the key range, so that every step issues the
 // same number of loads and the wait count stays exact -- then the scores
 // of t+1, the probabilities of t and P V of t, on this wave's NK keys of
-// each tile (starting koff bytes into it).
-template <int D, int NW, int NK>
-__device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D, NW> &lo, const bf16x8 *qf,
+// each tile (starting koff bytes into it).  The last LW waves of the
+// workgroup issue the tile loads (chunk offsets in ldo); the others issue
+// none and so never wait for them.  The compiler waits for every load into
+// LDS still in flight before a transposing LDS read (it cannot tell which
+// bytes such a read touches), so a wave that issued the current step's
+// refill waits for it at its first V read of the step; with LW = NW / 2 the
+// loads come from the waves that run behind their SIMD partners and reach
+// that read latest.
+template <int D, int NW, int NK, int LW>
+__device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D, NW> &lo,
+                                          const LaneOffsets<D, LW> &ldo, const bf16x8 *qf,
                                           RowState<D> &st, int kv_begin, int ntiles, int koff, int key0,
                                           __amdgpu_buffer_rsrc_t none,
                                           LDS_AS char *__restrict__ K0, LDS_AS char *__restrict__ K1,
@@ -527,10 +535,12 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
                                           LDS_AS char *__restrict__ V0, LDS_AS char *__restrict__ V1,
                                           LDS_AS char *__restrict__ V2, LDS_AS char *__restrict__ V3) {
     constexpr int NKB = NK / 32, PS = NK / 16;
-    constexpr int PER_TILE = 2 * LaneOffsets<D, NW>::PER_THREAD;   // loads per wave per tile
+    constexpr int PER_TILE = 2 * LaneOffsets<D, LW>::PER_THREAD;   // loads per loading wave per tile
     auto load = [&](int i, bool f, LDS_AS char *kd, LDS_AS char *vd) {
-        dma_tile<D, NW>(f ? x.kr : none, lo.k_src, (kv_begin + i * BN) * x.k_stride, kd, x.wave);
-        dma_tile<D, NW>(f ? x.vr : none, lo.v_src, (kv_begin + i * BN) * x.v_stride, vd, x.wave);
+        if (x.wave >= NW - LW) {   // uniform
+            dma_tile<D, LW>(f ? x.kr : none, ldo.k_src, (kv_begin + i * BN) * x.k_stride, kd, x.wave - (NW - LW));
+            dma_tile<D, LW>(f ? x.vr : none, ldo.v_src, (kv_begin + i * BN) * x.v_stride, vd, x.wave - (NW - LW));
+        }
     };
     // The step at D = 128 (NK = 64, or 32 per key group), in three blocks:
     // the score MFMAs of tile t+1; the probabilities of tile t and their row
@@ -651,8 +661,9 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
             mask_tail<NK>(x, key0 + (t + 1) * BN, s_next);
         }
     };
-    // Q was loaded before this: the loads complete in issue order, so the
-    // count still outstanding names exactly what has landed.
+    // Q was loaded before this: the loads complete in issue order, so for a
+    // loading wave the count still outstanding names exactly what has landed
+    // (the others have no tile loads; the compiler waits for their Q).
     load(0, 0 < ntiles, K0, V0);
     load(1, 1 < ntiles, K1, V1);
     load(2, 2 < ntiles, K2, V2);
@@ -719,14 +730,19 @@ void fa_ring_kernel(const FaArgs a) {
     const __amdgpu_buffer_rsrc_t none = make_rsrc(a.k, 0);
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(a.q + b * a.q_sb + hh * a.q_sh, ((int64_t)(a.Sq - 1) * a.q_ss + D) * 2);
 
-    LaneOffsets<D, NW> lo;
+    // Tile loads come from the last LW waves: half of them for video
+    // self-attention, all of them when two key groups split each tile.
+    constexpr int LW = KG == 1 ? NW / 2 : NW;
+    const int lw = wave >= NW - LW ? wave - (NW - LW) : 0;
+    LaneOffsets<D, LW> ldo;
 #pragma unroll
-    for (int n = 0; n < LaneOffsets<D, NW>::PER_THREAD; ++n) {
-        const int idx = (n * NW + wave) * 64 + lane;
+    for (int n = 0; n < LaneOffsets<D, LW>::PER_THREAD; ++n) {
+        const int idx = (n * LW + lw) * 64 + lane;
         const int r = idx / NCH, p = idx % NCH;
-        lo.k_src[n] = r * x.k_stride + swz_k<D>(r, p) * 16;
-        lo.v_src[n] = r * x.v_stride + swz_v<D>(r, p) * 16;
+        ldo.k_src[n] = r * x.k_stride + swz_k<D>(r, p) * 16;
+        ldo.v_src[n] = r * x.v_stride + swz_v<D>(r, p) * 16;
     }
+    LaneOffsets<D, NW> lo;   // LDS read offsets
 #pragma unroll
     for (int k = 0; k < KS; ++k) lo.k_rd[k] = l32 * 2 * D + swz_k<D>(l32, 2 * k + hw) * 16;
     {
@@ -753,7 +769,7 @@ void fa_ring_kernel(const FaArgs a) {
     for (int i = 0; i < NDB; ++i) st.o[i] = f32x16{};
     st.m = -1e30f;
     st.l = 0.f;
-    ring_loop<D, NW, NK>(x, lo, qf, st, kv_begin, ntiles, group * NK * 2 * D, kv_begin + group * NK, none,
+    ring_loop<D, NW, NK, LW>(x, lo, ldo, qf, st, kv_begin, ntiles, group * NK * 2 * D, kv_begin + group * NK, none,
                          lds, lds + TILE, lds + 2 * TILE, lds + 3 * TILE,
                          lds + 4 * TILE, lds + 5 * TILE, lds + 6 * TILE, lds + 7 * TILE);
 
