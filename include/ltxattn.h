@@ -169,8 +169,12 @@ int ltxattn_last_hip_error(const ltxattn_handle *h);
 /* Per-kind timing with HIP events recorded on the stream each kind runs on.
  * ltxattn_profile_begin creates events for up to max_calls block calls
  * (created here, outside any timed region); each later block call (either
- * entry point) records events around the call, around every kind and one
- * after each kind's attention kernel when a combine kernel follows.
+ * entry point) records an event where the call starts, where each kind ends
+ * (a kind that follows another on the same stream starts at that event),
+ * one after each kind's attention kernel when a combine kernel follows, and,
+ * for the overlap entry point, where the audio side starts and where the
+ * call ends after the join: 7 events per sequential call at the headline
+ * shapes, each recorded between kernels that run back to back anyway.
  * ltxattn_profile_read waits for the recorded events and writes
  * LTXATTN_PROFILE_FLOATS floats per recorded call c < *n_calls (at most
  * max_calls), in milliseconds:

@@ -82,7 +82,7 @@ constexpr int BM_MAX = 256;      // most query rows per workgroup (8 waves x 32)
 constexpr int WAVES_PER_CU = 8;  // 2 per SIMD: the register budget of the attention kernel
 constexpr int NSPLIT_MAX = 16;   // key-range parts of a split work item
 constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
-constexpr int PROF_EVENTS = 14;         // per profiled block call: start, end, 3 per kind
+constexpr int PROF_EVENTS = 14;         // per profiled block call, at most: start, end, 3 per kind
 
 struct FaArgs {
     const __bf16 *q, *k, *v;
@@ -1112,9 +1112,12 @@ struct ltxattn_handle {
     hipStream_t side;
     hipEvent_t fork, join;
     int last_hip_error;
-    // profiling
+    // profiling: PROF_EVENTS events per call, and which of them bound what
     hipEvent_t *events;
-    bool *prof_mid;   // per call and kind: was the event after the attention kernel recorded
+    struct ProfCall {
+        int8_t start[4], mid[4], end[4];   // per kind; mid < 0: no combine kernel followed
+        int8_t first, last;                // the whole call
+    } *prof_calls;
     int prof_max, prof_n;
 };
 
@@ -1388,37 +1391,61 @@ int enqueue_block(ltxattn_handle *h, const ltxattn_block_io *io, hipStream_t st,
 
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return hip_fail(h, g.err);
+    // Profiling events go only where something starts or ends: a kind that
+    // follows another on the same stream starts at that kind's end event, and
+    // a sequential call ends at its last kind's.
     hipEvent_t *ev = nullptr;
-    bool *mid = nullptr;
+    ltxattn_handle::ProfCall *pc = nullptr;
     if (h->events && h->prof_n < h->prof_max) {
         ev = h->events + (int64_t)h->prof_n * PROF_EVENTS;
-        mid = h->prof_mid + (int64_t)h->prof_n * 4;
-        for (int n = 0; n < 4; ++n) mid[n] = false;
+        pc = h->prof_calls + h->prof_n;
         ++h->prof_n;
     }
-    hipError_t e;
-    if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail(h, e);
+    int n_ev = 0;
+    hipError_t e = hipSuccess;
+    auto record = [&](hipStream_t s) {   // the index of a newly recorded event
+        if (e == hipSuccess) e = hipEventRecord(ev[n_ev], s);
+        return (int8_t)n_ev++;
+    };
+    int8_t last_main = -1, last_side = -1;
+    if (ev) pc->first = last_main = record(st);
     if (overlap) {
-        if ((e = hipEventRecord(h->fork, st)) != hipSuccess) return hip_fail(h, e);
-        if ((e = hipStreamWaitEvent(h->side, h->fork, 0)) != hipSuccess) return hip_fail(h, e);
+        if (e == hipSuccess) e = hipEventRecord(h->fork, st);
+        if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
     }
+    if (e != hipSuccess) return hip_fail(h, e);
     for (int n = 0; n < 4; ++n) {
         const int k = KIND_ORDER[n];
-        hipStream_t ks = (overlap && k != LTXATTN_VIDEO_SELF) ? h->side : st;
-        if (ev && (e = hipEventRecord(ev[2 + 3 * k], ks)) != hipSuccess) return hip_fail(h, e);
-        if (on[k]) {
-            const int kv_len = (k == LTXATTN_AUDIO_SELF || k == LTXATTN_A2V) ? Lk : Sv;
-            const int rc = run_attention(h, io->attn[k], B, q_rows[k], kv_len, k == LTXATTN_V2A, ks,
-                                         ev ? ev[3 + 3 * k] : nullptr, mid ? &mid[k] : nullptr);
-            if (rc) return rc;
+        const bool main = !overlap || k == LTXATTN_VIDEO_SELF;
+        hipStream_t ks = main ? st : h->side;
+        int8_t &last = main ? last_main : last_side;
+        if (ev) {
+            pc->start[k] = last >= 0 ? last : record(ks);
+            pc->mid[k] = -1;
+            pc->end[k] = pc->start[k];
+            last = pc->start[k];
         }
-        if (ev && (e = hipEventRecord(ev[4 + 3 * k], ks)) != hipSuccess) return hip_fail(h, e);
+        if (e != hipSuccess) return hip_fail(h, e);
+        if (!on[k]) continue;
+        const int kv_len = (k == LTXATTN_AUDIO_SELF || k == LTXATTN_A2V) ? Lk : Sv;
+        bool mid_rec = false;
+        const int rc = run_attention(h, io->attn[k], B, q_rows[k], kv_len, k == LTXATTN_V2A, ks,
+                                     ev ? ev[n_ev] : nullptr, ev ? &mid_rec : nullptr);
+        if (rc) return rc;
+        if (ev) {
+            if (mid_rec) pc->mid[k] = (int8_t)n_ev++;
+            pc->end[k] = last = record(ks);
+            if (e != hipSuccess) return hip_fail(h, e);
+        }
     }
     if (overlap) {
         if ((e = hipEventRecord(h->join, h->side)) != hipSuccess) return hip_fail(h, e);
         if ((e = hipStreamWaitEvent(st, h->join, 0)) != hipSuccess) return hip_fail(h, e);
     }
-    if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return hip_fail(h, e);
+    if (ev) {
+        pc->last = overlap ? record(st) : last_main;
+        if (e != hipSuccess) return hip_fail(h, e);
+    }
     return LTXATTN_OK;
 }
 
@@ -1551,12 +1578,12 @@ int ltxattn_profile_begin(ltxattn_handle *h, int32_t max_calls) {
     if (g.err != hipSuccess) return hip_fail(h, g.err);
     if (h->events) ltxattn_profile_end(h);
     h->events = (hipEvent_t *)calloc((size_t)max_calls * PROF_EVENTS, sizeof(hipEvent_t));
-    h->prof_mid = (bool *)calloc((size_t)max_calls * 4, sizeof(bool));
-    if (!h->events || !h->prof_mid) {
+    h->prof_calls = (ltxattn_handle::ProfCall *)calloc((size_t)max_calls, sizeof(ltxattn_handle::ProfCall));
+    if (!h->events || !h->prof_calls) {
         free(h->events);
-        free(h->prof_mid);
+        free(h->prof_calls);
         h->events = nullptr;
-        h->prof_mid = nullptr;
+        h->prof_calls = nullptr;
         return LTXATTN_ERR_OOM;
     }
     for (int64_t i = 0; i < (int64_t)max_calls * PROF_EVENTS; ++i) {
@@ -1564,9 +1591,9 @@ int ltxattn_profile_begin(ltxattn_handle *h, int32_t max_calls) {
         if (e != hipSuccess) {
             for (int64_t j = 0; j < i; ++j) (void)hipEventDestroy(h->events[j]);
             free(h->events);
-            free(h->prof_mid);
+            free(h->prof_calls);
             h->events = nullptr;
-            h->prof_mid = nullptr;
+            h->prof_calls = nullptr;
             return hip_fail(h, e);
         }
     }
@@ -1582,20 +1609,23 @@ int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_
     const int n = h->prof_n < max_calls ? h->prof_n : max_calls;
     for (int c = 0; c < n; ++c) {
         hipEvent_t *ev = h->events + (int64_t)c * PROF_EVENTS;
-        hipError_t e = hipEventSynchronize(ev[1]);   // the call's end: after every kind
+        const ltxattn_handle::ProfCall &pc = h->prof_calls[c];
+        hipError_t e = hipEventSynchronize(ev[pc.last]);   // the call's end: after every kind
         if (e != hipSuccess) return hip_fail(h, e);
         float *out = ms + (int64_t)c * LTXATTN_PROFILE_FLOATS;
         for (int k = 0; k < 4; ++k) {
             float tot = 0.f, ker = 0.f;
-            if ((e = hipEventElapsedTime(&tot, ev[2 + 3 * k], ev[4 + 3 * k])) != hipSuccess) return hip_fail(h, e);
-            const bool m = h->prof_mid[(int64_t)c * 4 + k];
-            if ((e = hipEventElapsedTime(&ker, ev[2 + 3 * k], ev[m ? 3 + 3 * k : 4 + 3 * k])) != hipSuccess)
-                return hip_fail(h, e);
+            if (pc.end[k] != pc.start[k]) {   // else skipped: 0
+                if ((e = hipEventElapsedTime(&tot, ev[pc.start[k]], ev[pc.end[k]])) != hipSuccess) return hip_fail(h, e);
+                if ((e = hipEventElapsedTime(&ker, ev[pc.start[k]], ev[pc.mid[k] >= 0 ? pc.mid[k] : pc.end[k]]))
+                    != hipSuccess)
+                    return hip_fail(h, e);
+            }
             out[k] = tot;
             out[5 + k] = ker;
         }
         float tot = 0.f;
-        if ((e = hipEventElapsedTime(&tot, ev[0], ev[1])) != hipSuccess) return hip_fail(h, e);
+        if ((e = hipEventElapsedTime(&tot, ev[pc.first], ev[pc.last])) != hipSuccess) return hip_fail(h, e);
         out[4] = tot;
     }
     *n_calls = n;
@@ -1608,9 +1638,9 @@ int ltxattn_profile_end(ltxattn_handle *h) {
     DeviceGuard g(h->device);
     for (int64_t i = 0; i < (int64_t)h->prof_max * PROF_EVENTS; ++i) (void)hipEventDestroy(h->events[i]);
     free(h->events);
-    free(h->prof_mid);
+    free(h->prof_calls);
     h->events = nullptr;
-    h->prof_mid = nullptr;
+    h->prof_calls = nullptr;
     h->prof_max = h->prof_n = 0;
     return LTXATTN_OK;
 }
