@@ -558,6 +558,27 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
         constexpr int KS = D / 16, NDB = D / 32;
         constexpr int LA = 2;
         ring_barrier<PER_TILE>();
+        auto read_v = [&](int c, bf16x8 *op) {
+            const int k = c >> 1, dbp = c & 1;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const LDS_AS char *vp = v_cur + koff + lo.v_rd[2 * dbp + j] + k * 16 * 2 * D;
+                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)vp);
+                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vp + 8 * 2 * D));
+                op[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        };
+        // Two key groups (NK = 32): all of this tile's V operands fit in
+        // registers, so they are read before the refill is issued and the
+        // compiler's wait for loads into LDS before the next step's first
+        // transposed read covers a refill issued a whole step earlier.
+        constexpr bool PRE_V = NK < BN;
+        bf16x8 vall[PRE_V ? 2 * PS : 1][2];
+        if constexpr (PRE_V) {
+#pragma unroll
+            for (int c = 0; c < 2 * PS; ++c) read_v(c, vall[c]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         load(t + 3, t + 3 < ntiles, k_fill, v_fill);
 
         bf16x8 kop[LA + 1][NKB];
@@ -623,27 +644,27 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
         st.l += rsum;
 
         bf16x8 vop[LA + 1][2];
-        auto read_v = [&](int c, bf16x8 *op) {
-            const int k = c >> 1, dbp = c & 1;
+        if constexpr (PRE_V) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const LDS_AS char *vp = v_cur + koff + lo.v_rd[2 * dbp + j] + k * 16 * 2 * D;
-                const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)vp);
-                const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vp + 8 * 2 * D));
-                op[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            for (int c = 0; c < 2 * PS; ++c) {
+                const int k = c >> 1, dbp = c & 1;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    st.o[2 * dbp + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vall[c][j], pf[k], st.o[2 * dbp + j], 0, 0, 0);
             }
-        };
+        } else {
 #pragma unroll
-        for (int c = 0; c < LA; ++c) read_v(c, vop[c]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int c = 0; c < 2 * PS; ++c) {
-            if (c + LA < 2 * PS) read_v(c + LA, vop[(c + LA) % (LA + 1)]);
-            const int k = c >> 1, dbp = c & 1;
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                st.o[2 * dbp + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[c % (LA + 1)][j], pf[k], st.o[2 * dbp + j], 0, 0, 0);
+            for (int c = 0; c < LA; ++c) read_v(c, vop[c]);
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int c = 0; c < 2 * PS; ++c) {
+                if (c + LA < 2 * PS) read_v(c + LA, vop[(c + LA) % (LA + 1)]);
+                const int k = c >> 1, dbp = c & 1;
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    st.o[2 * dbp + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[c % (LA + 1)][j], pf[k], st.o[2 * dbp + j], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
     auto step = [&](const f32x16 *s_cur, f32x16 *s_next, int t, const LDS_AS char *k_next,
