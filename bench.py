@@ -104,6 +104,12 @@ def main():
     ap.add_argument("--cfg", type=int, default=3, help="workload (1..5); 3 is the headline block")
     ap.add_argument("--overlap", action="store_true",
                     help="ltxattn_block_attention_overlap: the audio-side kinds on a second stream")
+    ap.add_argument("--distinct", action="store_true",
+                    help="give every kind its own copies of its Q/K/V (no kind reads another's inputs "
+                         "through the caches)")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="write this many MiB of scratch between block calls (past the last-level "
+                         "cache); value then comes from the library's per-call events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -137,17 +143,28 @@ def main():
     outs = {k: torch.empty_like(dev["video_q"] if k in ("video_self", "a2v") else dev["audio_q"])
             for k in KINDS}
     stream = torch.cuda.current_stream()
-    io = ba.make_io(dev, w.audio_kv_len, outs)
+    kind_inputs = None
+    if args.distinct:
+        pairs = {"video_self": ("video_q", "video_k", "video_v"), "audio_self": ("audio_q", "audio_k", "audio_v"),
+                 "a2v": ("video_q", "audio_k", "audio_v"), "v2a": ("audio_q", "video_k", "video_v")}
+        kind_inputs = {k: tuple(dev[n].clone() for n in names) for k, names in pairs.items()}
+    io = ba.make_io(dev, w.audio_kv_len, outs, kind_inputs)
+    scratch = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device="cuda:0")
+               if args.flush_mib else None)
 
     block = lt.ltxattn_block_attention_overlap if args.overlap else lt.ltxattn_block_attention
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
+        if scratch is not None:
+            scratch.fill_(float(i))
         block(ba.handle, io, stream.cuda_stream)
     torch.cuda.synchronize()
 
     lt.ltxattn_profile_begin(ba.handle, args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(float(i))
         block(ba.handle, io, stream.cuda_stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -160,6 +177,8 @@ def main():
     flops = synth.attention_flops(w)
     nbytes = synth.attention_bytes(w)
     ms_step = wall * 1e3 / args.steps
+    if scratch is not None:   # the flush is not the block's work: time the calls by their events
+        ms_step = float(np.mean([r["total"] for r in rec]))
     value = sum(flops.values()) / (ms_step * 1e-3) / 1e12
     kind_ms = {k: float(np.mean([r[k] for r in rec])) for k in KINDS}
     kernel_ms = {k: float(np.mean([r["kernel"][k] for r in rec])) for k in KINDS}
@@ -192,7 +211,9 @@ def main():
                    "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
                    "video_tokens": w.video_len, "audio_tokens": w.audio_kv_len,
                    "audio_buffer_rows": w.audio_len, "parallelism": "none (1 GPU)",
-                 "schedule": "overlap" if args.overlap else "sequential"},
+                 "schedule": "overlap" if args.overlap else "sequential",
+                 "inputs": "distinct per kind" if args.distinct else "two stream triples",
+                 "flush_mib_between_calls": args.flush_mib},
         "kinds": kinds,
         "roofline": {"kernel": "fa_ring_kernel<128, 8, 1> (video self-attention)",
                      "bound": "mfma", "achieved": round(achieved, 2),

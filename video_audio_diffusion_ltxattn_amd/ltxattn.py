@@ -154,7 +154,7 @@ def ltxattn_profile_begin(h, max_calls: int) -> None:
 
 
 def ltxattn_profile_read(h, max_calls: int):
-    """Per recorded call: {kind: ms incl. its V transpose, 'total': ms,
+    """Per recorded call: {kind: ms of all its kernels, 'total': ms,
     'kernel': {kind: ms of the attention kernels only}}."""
     nf = LTXATTN_PROFILE_FLOATS
     buf = (ctypes.c_float * (nf * max_calls))()
@@ -214,8 +214,9 @@ class BlockAttention:
         except Exception:
             pass
 
-    def make_io(self, streams: dict, audio_kv_len: int, outs: dict) -> ltxattn_block_io:
-        """streams: video_q/k/v, audio_q/k/v tensors; outs: {kind name: output tensor}."""
+    def make_io(self, streams: dict, audio_kv_len: int, outs: dict, inputs: dict = None) -> ltxattn_block_io:
+        """streams: video_q/k/v, audio_q/k/v tensors; outs: {kind name: output tensor};
+        inputs: optional {kind name: (q, k, v)} replacing that kind's stream tensors."""
         vq, vk, vv = streams["video_q"], streams["video_k"], streams["video_v"]
         aq, ak, av = streams["audio_q"], streams["audio_k"], streams["audio_v"]
         io = ltxattn_block_io()
@@ -223,6 +224,7 @@ class BlockAttention:
         io.audio_len, io.audio_kv_len = aq.shape[1], int(audio_kv_len)
         pairs = {"video_self": (vq, vk, vv), "audio_self": (aq, ak, av),
                  "a2v": (vq, ak, av), "v2a": (aq, vk, vv)}
+        pairs.update(inputs or {})
         for name, o in outs.items():
             q, k, v = pairs[name]
             io.attn[KIND_INDEX[name]] = ltxattn_attn_io(tensor_desc(q), tensor_desc(k),
