@@ -876,7 +876,8 @@ void fa_ring_kernel(const FaArgs a) {
 // the same slot for 16-byte-per-lane row stores; the next tile's Q is
 // fetched after the stores, the other wave of the SIMD computing meanwhile
 // (STAGED, 8 waves, D = 128).  Otherwise (more keys than leave room for the
-// slots, or D = 64) 4 waves take Q straight into registers, one tile ahead.
+// slots, or D = 64) the waves -- 8 at D = 128 for long query streams, two
+// per SIMD, else 4 -- take Q straight into registers, one tile ahead.
 // No workgroup barrier is needed except when the head changes.
 constexpr int KVRES_SLOT = 32 * 128 * 2;   // one wave's 32 rows of Q or O at D = 128 (8 KB)
 
@@ -1191,14 +1192,14 @@ int run_resident_kv(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq,
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int nkt = ceil_div(kv_len, BN);
     const size_t kv_lds = (size_t)nkt * 2 * BN * D * 2;
-    // Row-staged Q/O: 8 waves x one 8 KB slot when the keys leave room for
-    // that, else 4 unstaged waves (operands straight from HBM into registers).
-    int nw = 4;
-    bool staged = false;
-    if (D == 128 && kv_lds + 8 * KVRES_SLOT <= LDS_BYTES) {
-        nw = 8;
-        staged = true;
-    }
+    // D = 128: 8 waves, two per SIMD, with Q and O rows staged through one
+    // 8 KB slot per wave when the keys leave room for the slots, else with
+    // Q straight from HBM into registers (up to 256 keys: 128 KB of K/V) --
+    // or 4 such waves when 256-query items would leave most CUs idle (a
+    // short query stream such as audio self-attention).  D = 64: 4 unstaged
+    // waves.
+    const bool staged = D == 128 && kv_lds + 8 * KVRES_SLOT <= LDS_BYTES;
+    const int nw = staged || (D == 128 && (int64_t)B * H * ceil_div(Sq, 256) >= h->num_cus) ? 8 : 4;
     const size_t lds = kv_lds + (staged ? (size_t)8 * KVRES_SLOT : 0);
     a.n_qtiles = ceil_div(Sq, 32 * nw);
     const int items = B * H * a.n_qtiles;
@@ -1209,6 +1210,8 @@ int run_resident_kv(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq,
     a.total = a.groups * per_group;
     if (D == 128 && staged)
         hipLaunchKernelGGL((fa_kvres_kernel<128, 8, true>), dim3(a.total), dim3(512), lds, st, a);
+    else if (D == 128 && nw == 8)
+        hipLaunchKernelGGL((fa_kvres_kernel<128, 8, false>), dim3(a.total), dim3(512), lds, st, a);
     else if (D == 128) hipLaunchKernelGGL((fa_kvres_kernel<128, 4, false>), dim3(a.total), dim3(256), lds, st, a);
     else hipLaunchKernelGGL((fa_kvres_kernel<64, 4, false>), dim3(a.total), dim3(256), lds, st, a);
     const hipError_t e = hipGetLastError();
@@ -1529,6 +1532,9 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
     // staged, the Q/O row slots) in LDS: allow it all of a CU's LDS.
     e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<128, 8, true>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<128, 8, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
     if (e == hipSuccess)
         e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<128, 4, false>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
