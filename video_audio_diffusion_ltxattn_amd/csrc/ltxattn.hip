@@ -40,17 +40,22 @@
 //  * Kernels per kind (one block call launches them in this order):
 //      video self   fa_ring_kernel<D, 8, 1>: 256-query items, one 8-wave
 //                   workgroup per CU, a 4-stage K/V ring in LDS with
-//                   partial load waits, a software-pipelined step (score
-//                   MFMAs of tile t+1 interleaved with the exponentials of
-//                   tile t).  The items of an incomplete last round run as
+//                   partial load waits, loaded by the four waves that run
+//                   behind their SIMD partners; each step is the score
+//                   MFMAs of tile t+1, the probabilities of tile t (against
+//                   the max in use, checked by their row sums) and its P V
+//                   MFMAs.  The items of an incomplete last round run as
 //                   key-range halves so the round fills its XCD.
 //      v2a          fa_ring_kernel<D, 8, 2>: every 128-query item (all the
 //                   audio queries of a head) split over the video keys, one
 //                   part per CU; two 4-wave groups take the two key halves
-//                   of each tile and merge in LDS; then fa_combine_kernel.
+//                   of each tile (a wave reads all of its V operands before
+//                   the step's refill) and merge in LDS; then
+//                   fa_combine_kernel.
 //      a2v, audio   fa_kvres_kernel: the few hundred audio keys of a head
 //      self         stay in LDS while the query tiles stream past; Q and O
-//                   move as whole rows through per-wave LDS slots.
+//                   move as whole rows through per-wave LDS slots (or Q
+//                   straight into registers when the keys fill the LDS).
 //      other shapes fa_fwd_kernel<D, 4> (two-buffer pipeline, 128-query
 //                   items) for long key streams that the cases above do
 //                   not cover, e.g. D = 64 or short video.
