@@ -116,20 +116,37 @@ def test_full_size_sampled(lt, torch, cfg):
         assert np.all(o <= hi) and np.all(o >= lo), f"cfg{cfg} {k}: output outside hull of valid V"
 
 
-def test_tail_round_split(lt, torch):
-    """8 heads x 9216 video queries = 288 work items of 256 queries.  On a
-    256-CU MI355X each XCD's group holds one head's 36 items and runs 32 at a
-    time, so the last 4 query tiles of each head (rows 8192..9215) run as
-    key-range parts merged by the combine kernel.  Rows there and elsewhere
-    must match."""
-    w = synth.Workload(31, "tail split", 1, 8, 128, 9216, 64, 64)
+TAIL_SPLITS = [
+    # 8 heads x 9216 video queries = 288 work items of 256 queries.  On a
+    # 256-CU MI355X each XCD's group holds one head's 36 items and runs 32 at
+    # a time, so the last 4 query tiles of each head (rows 8192..9215) run as
+    # 8 key-range parts, dealt after the whole items.
+    (synth.Workload(31, "tail split, 8 parts", 1, 8, 128, 9216, 64, 64), range(8), (8192, 9216)),
+    # 16 heads x 6144 = 384 items, 48 per XCD group: its last 16 (query tiles
+    # 8..23 of the odd heads, rows 2048..6143) run as two key halves on half
+    # of the group's CUs, the first halves dealt before the whole items and
+    # the second halves after them.
+    (synth.Workload(32, "tail split, 2 parts staggered", 1, 16, 128, 6144, 64, 64), range(1, 16, 2),
+     (2048, 6144)),
+]
+
+
+@pytest.mark.parametrize("w,split_heads,split_rows", TAIL_SPLITS, ids=lambda x: getattr(x, "name", None))
+def test_tail_round_split(lt, torch, w, split_heads, split_rows):
+    """Rows of the split items and of whole items must match the oracle."""
     inputs = synth.make_block_inputs(w)
     got = run_block(lt, torch, w, inputs, kinds=("video_self",))
-    rng = np.random.default_rng(31)
+    rng = np.random.default_rng(w.cfg)
+    lo, hi = split_rows
     rows = []
     for h in range(w.heads):
-        for i in list(rng.integers(8192, 9216, 6)) + [8192, 9215, int(rng.integers(0, 8192))]:
-            rows.append((0, h, int(i)))
+        if h in split_heads:
+            picks = list(rng.integers(lo, hi, 6)) + [lo, hi - 1]
+            if lo > 0:
+                picks.append(int(rng.integers(0, lo)))
+        else:
+            picks = list(rng.integers(0, w.video_len, 3))
+        rows += [(0, h, int(i)) for i in picks]
     rows = np.array(rows, np.int64)
     want = oracle.block_attention_rows(inputs, w.audio_kv_len, {"video_self": rows})["video_self"]
     compare(got["video_self"][rows[:, 0], rows[:, 2], rows[:, 1], :], want, "tail-split rows")
