@@ -10,7 +10,9 @@ seeded synthetic bf16 tensors already resident in HBM.
 Prints one JSON line.  ``value`` is the block's algorithmic attention FLOPs
 (4*B*H*Sq*Sk_valid*D summed over the four kinds) per second of step time.
 ``roofline`` describes the dominant kernel (video self-attention), timed
-with HIP events the library records on the stream it launches on.
+with HIP events the library records on the stream it launches on; in the
+timed region only that kind's events are recorded.  ``kinds`` comes from a
+separate, untimed pass that records every kind's boundaries.
 ``cpu_baseline`` is the double-precision oracle on a bounded sample of the
 same work on this host's cores.
 """
@@ -110,6 +112,8 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write this many MiB of scratch between block calls (past the last-level "
                          "cache); value then comes from the library's per-call events")
+    ap.add_argument("--kind-calls", type=int, default=10,
+                    help="untimed block calls, after the timed ones, that give the per-kind times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -159,7 +163,13 @@ def main():
         block(ba.handle, io, stream.cuda_stream)
     torch.cuda.synchronize()
 
-    lt.ltxattn_profile_begin(ba.handle, args.steps)
+    # Timed region: events only around video self-attention (3 per call),
+    # enough for the roofline's kernel time; with a flush between calls the
+    # whole call is timed by its events, so every kind is recorded.
+    if scratch is not None:
+        lt.ltxattn_profile_begin(ba.handle, args.steps)
+    else:
+        lt.ltxattn_profile_begin_kinds(ba.handle, args.steps, ["video_self"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -170,6 +180,16 @@ def main():
     wall = time.perf_counter() - t0
     rec = lt.ltxattn_profile_read(ba.handle, args.steps)
     lt.ltxattn_profile_end(ba.handle)
+    # Per-kind breakdown: a separate pass with every kind's boundaries recorded.
+    if scratch is None:
+        lt.ltxattn_profile_begin(ba.handle, args.kind_calls)
+        for i in range(args.kind_calls):
+            block(ba.handle, io, stream.cuda_stream)
+        torch.cuda.synchronize()
+        rec_kinds = lt.ltxattn_profile_read(ba.handle, args.kind_calls)
+        lt.ltxattn_profile_end(ba.handle)
+    else:
+        rec_kinds = rec
 
     for k in KINDS:
         assert torch.isfinite(outs[k].float()).all(), f"{k}: non-finite output"
@@ -180,8 +200,8 @@ def main():
     if scratch is not None:   # the flush is not the block's work: time the calls by their events
         ms_step = float(np.mean([r["total"] for r in rec]))
     value = sum(flops.values()) / (ms_step * 1e-3) / 1e12
-    kind_ms = {k: float(np.mean([r[k] for r in rec])) for k in KINDS}
-    kernel_ms = {k: float(np.mean([r["kernel"][k] for r in rec])) for k in KINDS}
+    kind_ms = {k: float(np.mean([r[k] for r in rec_kinds])) for k in KINDS}
+    kernel_ms = {k: float(np.mean([r["kernel"][k] for r in rec_kinds])) for k in KINDS}
     kinds = {}
     for k in KINDS:
         t = kind_ms[k] * 1e-3
@@ -191,7 +211,8 @@ def main():
                     "pct_bf16_peak": round(100 * flops[k] / t / 1e12 / PEAK_BF16_TFLOPS, 2),
                     "hbm_gbs": round(nbytes[k] / t / 1e9, 1),
                     "pct_hbm_peak": round(100 * nbytes[k] / t / 1e9 / PEAK_HBM_GBS, 2)}
-    vs_ms = kernel_ms["video_self"]   # the attention kernel alone (its tail combine excluded)
+    # The attention kernel alone (its tail combine excluded), timed region
+    vs_ms = float(np.mean([r["kernel"]["video_self"] for r in rec]))
     achieved = flops["video_self"] / (vs_ms * 1e-3) / 1e12
     out = {
         "metric": METRIC,

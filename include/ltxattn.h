@@ -183,9 +183,17 @@ int ltxattn_last_hip_error(const ltxattn_handle *h);
  *   ms[c*9 + 5 + kind]  that kind's attention kernel alone, without the
  *                       combine kernel that merges key-range parts.
  * ltxattn_profile_end stops recording and frees the events.
- * Errors: INVALID_ARG (null pointer, max_calls < 1), HIP. */
+ * ltxattn_profile_begin_kinds records only the kinds whose bit (1 << kind)
+ * is set in kind_mask (1..15), so that a timed loop carries only the events
+ * it needs (each costs a few microseconds of device time): 3 per call for
+ * VIDEO_SELF alone at the headline shapes.  Kinds outside the mask, and the
+ * whole-call figure unless kind_mask is 15, read as NaN.
+ * ltxattn_profile_begin(h, n) is ltxattn_profile_begin_kinds(h, n, 15).
+ * Errors: INVALID_ARG (null pointer, max_calls < 1, kind_mask out of
+ * range), HIP. */
 #define LTXATTN_PROFILE_FLOATS 9
 int ltxattn_profile_begin(ltxattn_handle *h, int32_t max_calls);
+int ltxattn_profile_begin_kinds(ltxattn_handle *h, int32_t max_calls, uint32_t kind_mask);
 int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_t *n_calls);
 int ltxattn_profile_end(ltxattn_handle *h);
 

@@ -61,6 +61,7 @@ def test_null_handles():
     assert lt._lib.ltxattn_block_attention_overlap(None, ctypes.byref(io), None) == lt.LTXATTN_ERR_INVALID_ARG
     assert lt._lib.ltxattn_destroy(None) == lt.LTXATTN_OK
     assert lt._lib.ltxattn_profile_begin(None, 4) == lt.LTXATTN_ERR_INVALID_ARG
+    assert lt._lib.ltxattn_profile_begin_kinds(None, 4, 1) == lt.LTXATTN_ERR_INVALID_ARG
     assert lt._lib.ltxattn_last_hip_error(None) == 0
 
 

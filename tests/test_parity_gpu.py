@@ -280,6 +280,32 @@ def test_profile_events(lt, torch, overlap):
     ba.close()
 
 
+@pytest.mark.parametrize("overlap", [False, True])
+@pytest.mark.parametrize("kinds", [("video_self",), ("a2v", "v2a"), ("audio_self",)])
+def test_profile_selected_kinds(lt, torch, kinds, overlap):
+    """Recording a subset of kinds: those read as times, the rest and the
+    whole-call figure as NaN; a kind after an unrecorded one gets its own start."""
+    w = RAGGED[[r.cfg for r in RAGGED].index(17)]
+    dev = {n: to_device(a) for n, a in synth.make_block_inputs(w).items()}
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
+    lt.ltxattn_profile_begin_kinds(ba.handle, 3, kinds)
+    for _ in range(3):
+        ba(dev, w.audio_kv_len, overlap=overlap)
+    rec = lt.ltxattn_profile_read(ba.handle, 3)
+    lt.ltxattn_profile_end(ba.handle)
+    assert len(rec) == 3
+    for r in rec:
+        assert np.isnan(r["total"])
+        for k in KINDS:
+            if k in kinds:
+                assert 0 < r["kernel"][k] <= r[k] + 1e-3
+            else:
+                assert np.isnan(r[k]) and np.isnan(r["kernel"][k])
+    with pytest.raises(lt.LtxattnError):
+        lt.ltxattn_profile_begin_kinds(ba.handle, 3, [])
+    ba.close()
+
+
 def test_create_on_missing_device(lt, torch):
     cfg = lt.ltxattn_config(99, 4, 64, 1, 16, 16)
     with pytest.raises(lt.LtxattnError) as e:

@@ -1165,10 +1165,13 @@ struct ltxattn_handle {
     // profiling: PROF_EVENTS events per call, and which of them bound what
     hipEvent_t *events;
     struct ProfCall {
-        int8_t start[4], mid[4], end[4];   // per kind; mid < 0: no combine kernel followed
-        int8_t first, last;                // the whole call
+        int8_t start[4], mid[4], end[4];   // per kind; mid < 0: no combine kernel followed;
+                                           // start < 0: kind not recorded
+        int8_t first, last;                // the whole call (first < 0: not recorded)
+        int8_t sync;                       // the call's last recorded event
     } *prof_calls;
     int prof_max, prof_n;
+    unsigned prof_kinds;                   // bit k: kind k is recorded
 };
 
 namespace {
@@ -1430,10 +1433,11 @@ int validate_block(const ltxattn_config &caps, const ltxattn_block_io *io, bool 
 // handle's side stream instead, forked from the caller's stream at the
 // start of the call and joined back into it at the end, so the call stays
 // one ordered unit on the caller's stream (and can be captured into a HIP
-// graph from it).  Profiling events, if on: 0 and 1 open and close the call
-// on the caller's stream; 2 + 3k, 3 + 3k, 4 + 3k are the start of kind k,
-// the end of its attention kernel when a combine kernel follows, and its
-// end, on the stream that runs it.
+// graph from it).  Profiling events, if on, are recorded in enqueue order
+// and indexed per call by ProfCall: the call's start and end (when every
+// kind is recorded), and for each recorded kind its start, the end of its
+// attention kernel when a combine kernel follows, and its end, on the
+// stream that runs it.
 int enqueue_block(ltxattn_handle *h, const ltxattn_block_io *io, hipStream_t st, bool overlap) {
     if (!h || !io) return LTXATTN_ERR_INVALID_ARG;
     const ltxattn_config caps = {h->device, h->heads, h->head_dim, h->max_batch, h->max_video_len,
@@ -1462,8 +1466,11 @@ int enqueue_block(ltxattn_handle *h, const ltxattn_block_io *io, hipStream_t st,
         if (e == hipSuccess) e = hipEventRecord(ev[n_ev], s);
         return (int8_t)n_ev++;
     };
+    // With every kind recorded the call's own first and last events are
+    // kept as well (its total); with a subset only those kinds' boundaries.
+    const bool all = h->prof_kinds == 0xFu;
     int8_t last_main = -1, last_side = -1;
-    if (ev) pc->first = last_main = record(st);
+    if (ev) pc->first = last_main = all ? record(st) : (int8_t)-1;
     if (overlap) {
         if (e == hipSuccess) e = hipEventRecord(h->fork, st);
         if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
@@ -1474,23 +1481,26 @@ int enqueue_block(ltxattn_handle *h, const ltxattn_block_io *io, hipStream_t st,
         const bool main = !overlap || k == LTXATTN_VIDEO_SELF;
         hipStream_t ks = main ? st : h->side;
         int8_t &last = main ? last_main : last_side;
+        const bool rec_k = ev && (h->prof_kinds >> k & 1u);
         if (ev) {
-            pc->start[k] = last >= 0 ? last : record(ks);
+            pc->start[k] = rec_k ? (last >= 0 ? last : record(ks)) : (int8_t)-1;
             pc->mid[k] = -1;
             pc->end[k] = pc->start[k];
-            last = pc->start[k];
+            if (rec_k) last = pc->start[k];
         }
         if (e != hipSuccess) return hip_fail(h, e);
         if (!on[k]) continue;
         const int kv_len = (k == LTXATTN_AUDIO_SELF || k == LTXATTN_A2V) ? Lk : Sv;
         bool mid_rec = false;
         const int rc = run_attention(h, io->attn[k], B, q_rows[k], kv_len, k == LTXATTN_V2A, ks,
-                                     ev ? ev[n_ev] : nullptr, ev ? &mid_rec : nullptr);
+                                     rec_k ? ev[n_ev] : nullptr, rec_k ? &mid_rec : nullptr);
         if (rc) return rc;
-        if (ev) {
+        if (rec_k) {
             if (mid_rec) pc->mid[k] = (int8_t)n_ev++;
             pc->end[k] = last = record(ks);
             if (e != hipSuccess) return hip_fail(h, e);
+        } else {
+            last = -1;   // an unrecorded kind ran since: the next kind records its own start
         }
     }
     if (overlap) {
@@ -1498,7 +1508,8 @@ int enqueue_block(ltxattn_handle *h, const ltxattn_block_io *io, hipStream_t st,
         if ((e = hipStreamWaitEvent(st, h->join, 0)) != hipSuccess) return hip_fail(h, e);
     }
     if (ev) {
-        pc->last = overlap ? record(st) : last_main;
+        pc->last = !all ? (int8_t)-1 : overlap ? record(st) : last_main;
+        pc->sync = (int8_t)(n_ev - 1);
         if (e != hipSuccess) return hip_fail(h, e);
     }
     return LTXATTN_OK;
@@ -1631,7 +1642,11 @@ int ltxattn_block_attention_overlap(ltxattn_handle *h, const ltxattn_block_io *i
 }
 
 int ltxattn_profile_begin(ltxattn_handle *h, int32_t max_calls) {
-    if (!h || max_calls < 1) return LTXATTN_ERR_INVALID_ARG;
+    return ltxattn_profile_begin_kinds(h, max_calls, 0xFu);
+}
+
+int ltxattn_profile_begin_kinds(ltxattn_handle *h, int32_t max_calls, uint32_t kind_mask) {
+    if (!h || max_calls < 1 || kind_mask == 0 || kind_mask > 0xFu) return LTXATTN_ERR_INVALID_ARG;
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return hip_fail(h, g.err);
     if (h->events) ltxattn_profile_end(h);
@@ -1657,6 +1672,7 @@ int ltxattn_profile_begin(ltxattn_handle *h, int32_t max_calls) {
     }
     h->prof_max = max_calls;
     h->prof_n = 0;
+    h->prof_kinds = kind_mask;
     return LTXATTN_OK;
 }
 
@@ -1668,11 +1684,14 @@ int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_
     for (int c = 0; c < n; ++c) {
         hipEvent_t *ev = h->events + (int64_t)c * PROF_EVENTS;
         const ltxattn_handle::ProfCall &pc = h->prof_calls[c];
-        hipError_t e = hipEventSynchronize(ev[pc.last]);   // the call's end: after every kind
-        if (e != hipSuccess) return hip_fail(h, e);
         float *out = ms + (int64_t)c * LTXATTN_PROFILE_FLOATS;
+        for (int i = 0; i < LTXATTN_PROFILE_FLOATS; ++i) out[i] = NAN;
+        if (pc.sync < 0) continue;                          // no recorded kind ran
+        hipError_t e = hipEventSynchronize(ev[pc.sync]);   // the call's last recorded event
+        if (e != hipSuccess) return hip_fail(h, e);
         for (int k = 0; k < 4; ++k) {
             float tot = 0.f, ker = 0.f;
+            if (pc.start[k] < 0) continue;                  // not recorded: NaN
             if (pc.end[k] != pc.start[k]) {   // else skipped: 0
                 if ((e = hipEventElapsedTime(&tot, ev[pc.start[k]], ev[pc.end[k]])) != hipSuccess) return hip_fail(h, e);
                 if ((e = hipEventElapsedTime(&ker, ev[pc.start[k]], ev[pc.mid[k] >= 0 ? pc.mid[k] : pc.end[k]]))
@@ -1682,9 +1701,11 @@ int ltxattn_profile_read(ltxattn_handle *h, float *ms, int32_t max_calls, int32_
             out[k] = tot;
             out[5 + k] = ker;
         }
-        float tot = 0.f;
-        if ((e = hipEventElapsedTime(&tot, ev[pc.first], ev[pc.last])) != hipSuccess) return hip_fail(h, e);
-        out[4] = tot;
+        if (pc.first >= 0) {
+            float tot = 0.f;
+            if ((e = hipEventElapsedTime(&tot, ev[pc.first], ev[pc.last])) != hipSuccess) return hip_fail(h, e);
+            out[4] = tot;
+        }
     }
     *n_calls = n;
     return LTXATTN_OK;

@@ -87,6 +87,7 @@ def _load():
         "ltxattn_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "ltxattn_last_hip_error": ([P], ctypes.c_int),
         "ltxattn_profile_begin": ([P, ctypes.c_int32], ctypes.c_int),
+        "ltxattn_profile_begin_kinds": ([P, ctypes.c_int32, ctypes.c_uint32], ctypes.c_int),
         "ltxattn_profile_read": ([P, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
                                   ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
         "ltxattn_profile_end": ([P], ctypes.c_int),
@@ -102,7 +103,8 @@ _lib = _load()
 EXPORTED = ("ltxattn_create", "ltxattn_block_attention", "ltxattn_block_attention_overlap",
             "ltxattn_check_block",
             "ltxattn_destroy", "ltxattn_status_string", "ltxattn_last_hip_error",
-            "ltxattn_profile_begin", "ltxattn_profile_read", "ltxattn_profile_end")
+            "ltxattn_profile_begin", "ltxattn_profile_begin_kinds", "ltxattn_profile_read",
+            "ltxattn_profile_end")
 
 
 # ------------------------------------------------------------- C-named calls
@@ -153,9 +155,20 @@ def ltxattn_profile_begin(h, max_calls: int) -> None:
         raise LtxattnError(rc, "ltxattn_profile_begin")
 
 
+def ltxattn_profile_begin_kinds(h, max_calls: int, kinds) -> None:
+    """Record events for the named kinds only (others, and 'total' unless all
+    four are named, read as NaN)."""
+    mask = 0
+    for k in kinds:
+        mask |= 1 << KIND_INDEX[k]
+    rc = _lib.ltxattn_profile_begin_kinds(h, int(max_calls), mask)
+    if rc != LTXATTN_OK:
+        raise LtxattnError(rc, "ltxattn_profile_begin_kinds")
+
+
 def ltxattn_profile_read(h, max_calls: int):
     """Per recorded call: {kind: ms of all its kernels, 'total': ms,
-    'kernel': {kind: ms of the attention kernels only}}."""
+    'kernel': {kind: ms of the attention kernels only}}; NaN where not recorded."""
     nf = LTXATTN_PROFILE_FLOATS
     buf = (ctypes.c_float * (nf * max_calls))()
     n = ctypes.c_int32()
