@@ -112,7 +112,7 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write this many MiB of scratch between block calls (past the last-level "
                          "cache); value then comes from the library's per-call events")
-    ap.add_argument("--kind-calls", type=int, default=10,
+    ap.add_argument("--kind-calls", type=int, default=20,
                     help="untimed block calls, after the timed ones, that give the per-kind times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -205,7 +205,10 @@ def main():
     kinds = {}
     for k in KINDS:
         t = kind_ms[k] * 1e-3
+        per_call = [r[k] for r in rec_kinds]
         kinds[k] = {"ms": round(kind_ms[k], 5),
+                    "median_ms": round(float(np.median(per_call)), 5),
+                    "min_ms": round(float(np.min(per_call)), 5),
                     "attention_kernels_ms": round(kernel_ms[k], 5),
                     "tflops": round(flops[k] / t / 1e12, 2),
                     "pct_bf16_peak": round(100 * flops[k] / t / 1e12 / PEAK_BF16_TFLOPS, 2),
