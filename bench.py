@@ -111,7 +111,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed block calls first: a process's first ~12 calls run up to 20%% slower "
+                         "while the clocks ramp up")
     ap.add_argument("--cfg", type=int, default=3, help="workload (1..5); 3 is the headline block")
     ap.add_argument("--overlap", action="store_true",
                     help="ltxattn_block_attention_overlap: the audio-side kinds on a second stream")
