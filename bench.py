@@ -54,17 +54,30 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def measured_traffic():
+def workload_key(w: synth.Workload) -> str:
+    return f"video {w.video_len}, H{w.heads}, D{w.head_dim}, B{w.batch}"
+
+
+def measured_traffic(w: synth.Workload):
     """HBM bytes per video-self launch from the committed rocprofv3 counter
-    runs, or None if they were taken on a different kernel source."""
+    runs, or None if they were taken on a different kernel source or a
+    different workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash() or t.get("workload") != workload_key(w):
         return None
     return t.get("bytes_per_launch")
+
+
+def video_kernel_name(w: synth.Workload) -> str:
+    """The kernel video self-attention runs on for this shape (the library's
+    choice: the ring kernel for long sequences at D = 128)."""
+    if w.head_dim == 128 and w.video_len >= 1024:
+        return "fa_ring_kernel<128, 8, 1> (video self-attention)"
+    return "video self-attention kernel (fa_kvres_kernel or fa_fwd_kernel at this shape)"
 
 
 def cpu_baseline(inputs: dict, w: synth.Workload, min_s: float, max_s: float) -> dict:
@@ -250,11 +263,11 @@ def main():
                  "inputs": "distinct per kind" if args.distinct else "two stream triples",
                  "flush_mib_between_calls": args.flush_mib},
         "kinds": kinds,
-        "roofline": {"kernel": "fa_ring_kernel<128, 8, 1> (video self-attention)",
+        "roofline": {"kernel": video_kernel_name(w),
                      "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(),
+                     "traffic": measured_traffic(w),
                      "avg_launch_ms": round(vs_ms, 5)},
     }
     if not args.no_cpu_baseline:

@@ -61,14 +61,16 @@ def test_traffic_only_for_the_code_it_was_taken_on(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
     traffic = tmp_path / "t.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(traffic))
-    assert bench.measured_traffic() is None                       # no file
+    w = synth.WORKLOADS[3]
+    assert bench.measured_traffic(w) is None                      # no file
     traffic.write_text(json.dumps({"kernel_source_sha256_16": bench.kernel_source_hash(),
-                                   "bytes_per_launch": 123}))
-    assert bench.measured_traffic() == 123
+                                   "workload": bench.workload_key(w), "bytes_per_launch": 123}))
+    assert bench.measured_traffic(w) == 123
+    assert bench.measured_traffic(synth.WORKLOADS[2]) is None     # taken on another workload
     src.write_text("int f() { return 2; }\n")                    # the kernel changed since
-    assert bench.measured_traffic() is None
+    assert bench.measured_traffic(w) is None
     traffic.write_text("{not json")
-    assert bench.measured_traffic() is None
+    assert bench.measured_traffic(w) is None
 
 
 def test_committed_traffic_file_names_its_source():
@@ -76,3 +78,9 @@ def test_committed_traffic_file_names_its_source():
         t = json.load(f)
     assert len(t["kernel_source_sha256_16"]) == 16
     assert t["bytes_per_launch"] == t["fetch_bytes"] + t["write_bytes"]
+    assert t["workload"] == bench.workload_key(synth.WORKLOADS[3])   # the headline workload
+
+
+def test_roofline_kernel_name_follows_the_shape():
+    assert bench.video_kernel_name(synth.WORKLOADS[3]).startswith("fa_ring_kernel<128, 8, 1>")
+    assert not bench.video_kernel_name(synth.WORKLOADS[1]).startswith("fa_ring_kernel")   # 256 tokens, D = 64
