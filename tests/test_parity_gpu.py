@@ -200,6 +200,51 @@ def test_needles_at_boundaries(lt, torch):
         compare(got[k][r[:, 0], r[:, 2], r[:, 1], :], want[k], f"needle {k}", guard=False)
 
 
+def test_degenerate_logits(lt, torch):
+    """Q = 0: every logit is equal, so each output row is the mean of the valid V
+    rows (a closed form, computed here independently of the oracle).  Q and K
+    scaled by 30 (logits of several hundred): every output is finite and inside
+    the hull of the valid V rows, and rows whose top logit leads the next by more
+    than 20 (all but ~1e-9 of the weight on one key) match the oracle."""
+    w = synth.Workload(41, "degenerate", 1, 2, 128, 1100, 77, 70)   # ring kernel, ragged tails
+    base = synth.make_block_inputs(w)
+    Lk = w.audio_kv_len
+    v = {"video": synth.bits_to_f32(base["video_v"]).astype(np.float64),
+         "audio": synth.bits_to_f32(base["audio_v"]).astype(np.float64)[:, :Lk]}
+    keys_of = {"video_self": "video", "audio_self": "audio", "a2v": "audio", "v2a": "video"}
+
+    flat = dict(base)
+    flat["video_q"] = np.zeros_like(base["video_q"])
+    flat["audio_q"] = np.zeros_like(base["audio_q"])
+    got = run_block(lt, torch, w, flat)
+    for k in KINDS:
+        mean = v[keys_of[k]].mean(axis=1, keepdims=True)
+        compare(got[k], np.broadcast_to(mean, got[k].shape), f"Q = 0 {k}")
+
+    big = dict(base)
+    for n in ("video_q", "video_k", "audio_q", "audio_k"):
+        big[n] = synth.bf16_bits(synth.bits_to_f32(base[n]) * 30)
+    got = run_block(lt, torch, w, big)
+    want = oracle.block_attention(big, Lk)
+    q_of = {"video_self": "video", "audio_self": "audio", "a2v": "video", "v2a": "audio"}
+    for k in KINDS:
+        g = got[k]
+        assert np.isfinite(g).all(), k
+        vv = v[keys_of[k]]
+        lo, hi = vv.min(axis=1, keepdims=True), vv.max(axis=1, keepdims=True)
+        assert (g >= lo - 1e-2).all() and (g <= hi + 1e-2).all(), k
+        q = synth.bits_to_f32(big[q_of[k] + "_q"]).astype(np.float64)
+        kk = synth.bits_to_f32(big[keys_of[k] + "_k"]).astype(np.float64)
+        if keys_of[k] == "audio":
+            kk = kk[:, :Lk]
+        logits = np.einsum("bihd,bjhd->bhij", q, kk) / np.sqrt(w.head_dim)
+        top2 = np.sort(logits, axis=-1)[..., -2:]
+        sel = np.argwhere(top2[..., 1] - top2[..., 0] > 20)   # (b, h, i)
+        assert len(sel) > 0.5 * logits.shape[0] * logits.shape[1] * logits.shape[2], k
+        b, h, i = sel[:, 0], sel[:, 1], sel[:, 2]
+        compare(g[b, i, h], want[k][b, i, h], f"30x logits, one-hot rows {k}")
+
+
 def test_strided_layouts_and_guard_bands(lt, torch):
     """Inputs in [B, H, S, D] storage, outputs inside larger buffers: the
     kernels honour every stride and write nothing outside the output view."""
