@@ -245,6 +245,36 @@ def test_degenerate_logits(lt, torch):
         compare(g[b, i, h], want[k][b, i, h], f"30x logits, one-hot rows {k}")
 
 
+def test_distinct_tensors_per_kind(lt, torch):
+    """Each kind with its own Q/K/V (the ABI accepts per-kind tensors, not only
+    the two shared stream triples): every kind matches the oracle on its own
+    inputs, so no kind reads another kind's tensors."""
+    w = synth.Workload(42, "distinct per kind", 1, 2, 128, 1100, 77, 70)   # ring path, split v2a
+    stream = synth.make_block_inputs(w)
+    rng = np.random.default_rng(42)
+    rows = {"video": w.video_len, "audio": w.audio_len}
+    q_of = {"video_self": "video", "audio_self": "audio", "a2v": "video", "v2a": "audio"}
+    kv_of = {"video_self": "video", "audio_self": "audio", "a2v": "audio", "v2a": "video"}
+    shape = lambda s: (w.batch, rows[s], w.heads, w.head_dim)
+    own = {}
+    for k in KINDS:
+        own[k] = tuple(synth.bf16_bits(rng.standard_normal(shape(s)).astype(np.float32))
+                       for s in (q_of[k], kv_of[k], kv_of[k]))
+    dev = {n: to_device(a) for n, a in stream.items()}
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
+    outs = {k: torch.empty_like(dev[q_of[k] + "_q"]) for k in KINDS}
+    own_dev = {k: tuple(to_device(a) for a in own[k]) for k in KINDS}   # alive until the sync below
+    io = ba.make_io(dev, w.audio_kv_len, outs, inputs=own_dev)
+    lt.ltxattn_block_attention(ba.handle, io, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    del own_dev
+    for k in KINDS:
+        q, kk, vv = own[k]
+        want = oracle.attention(q, kk, vv, kv_len=w.audio_kv_len if kv_of[k] == "audio" else None)
+        compare(to_numpy(outs[k]), want, f"distinct inputs {k}")
+    ba.close()
+
+
 def test_strided_layouts_and_guard_bands(lt, torch):
     """Inputs in [B, H, S, D] storage, outputs inside larger buffers: the
     kernels honour every stride and write nothing outside the output view."""

@@ -229,7 +229,9 @@ class BlockAttention:
 
     def make_io(self, streams: dict, audio_kv_len: int, outs: dict, inputs: dict = None) -> ltxattn_block_io:
         """streams: video_q/k/v, audio_q/k/v tensors; outs: {kind name: output tensor};
-        inputs: optional {kind name: (q, k, v)} replacing that kind's stream tensors."""
+        inputs: optional {kind name: (q, k, v)} replacing that kind's stream tensors.
+        The struct holds raw device pointers: every tensor named here must stay
+        alive until the work enqueued with it has completed."""
         vq, vk, vv = streams["video_q"], streams["video_k"], streams["video_v"]
         aq, ak, av = streams["audio_q"], streams["audio_k"], streams["audio_v"]
         io = ltxattn_block_io()
