@@ -128,6 +128,10 @@ TAIL_SPLITS = [
     # the second halves after them.
     (synth.Workload(32, "tail split, 2 parts staggered", 1, 16, 128, 6144, 64, 64), range(1, 16, 2),
      (2048, 6144)),
+    # D = 64 takes fa_fwd_kernel (128-query items, two workgroups per CU): 8
+    # heads x 72 items, one head per XCD group of 64 slots, so each head's last
+    # 8 query tiles (rows 8192..9215) run as 8 key-range parts.
+    (synth.Workload(33, "tail split, D64 two-buffer kernel", 1, 8, 64, 9216, 64, 64), range(8), (8192, 9216)),
 ]
 
 
