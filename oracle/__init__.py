@@ -21,6 +21,12 @@ v2a           audio      video       all video tokens
 
 Audio keys at or beyond ``audio_kv_len`` are padding (the audio stream is
 padded, same PR, "Description") and get weight exactly zero.
+
+Gated attention (named among the DiT's parts by TensorRT-Model-Connect PR
+#1586, the commit onboarding LTX-2.5, which gives no gate formula): an
+optional gate of the output's shape, taken as given (already activated), is
+multiplied elementwise into each output row: o_gated[b, i, h, d] =
+gate[b, i, h, d] * o[b, i, h, d].
 """
 
 from __future__ import annotations
@@ -104,11 +110,20 @@ def _shapes(q, k, v, kv_len):
     return B, Sq, Sk, kv_len, H, D
 
 
-def attention(q, k, v, kv_len=None, threads=None, return_lse=False):
-    """softmax(q k^T / sqrt(D)) v over keys j < kv_len, in double.
+def _gate(gate, shape):
+    g = _as_f32(gate).astype(np.float64)
+    if g.shape != shape:
+        raise ValueError(f"gate shape {g.shape}, expected {shape}")
+    return g
 
-    q: [B, Sq, H, D]; k, v: [B, Sk, H, D] (bf16 bits or float32 values).
-    Returns o [B, Sq, H, D] float64 (and lse [B, Sq, H] if asked).
+
+def attention(q, k, v, kv_len=None, threads=None, return_lse=False, gate=None):
+    """softmax(q k^T / sqrt(D)) v over keys j < kv_len, in double, times
+    ``gate`` elementwise if given.
+
+    q: [B, Sq, H, D]; k, v: [B, Sk, H, D]; gate: [B, Sq, H, D] (bf16 bits or
+    float32 values).  Returns o [B, Sq, H, D] float64 (and lse [B, Sq, H] if
+    asked; the lse is the ungated softmax's).
     """
     q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
     B, Sq, Sk, L, H, D = _shapes(q, k, v, kv_len)
@@ -120,10 +135,12 @@ def attention(q, k, v, kv_len=None, threads=None, return_lse=False):
         threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle failed with {rc}")
+    if gate is not None:
+        out *= _gate(gate, out.shape)
     return (out, lse) if return_lse else out
 
 
-def attention_rows(q, k, v, rows, kv_len=None, threads=None, return_lse=False):
+def attention_rows(q, k, v, rows, kv_len=None, threads=None, return_lse=False, gate=None):
     """Same as :func:`attention` for selected rows only.
 
     rows: int array [n, 3] of (b, h, i).  Returns o [n, D] float64 (and lse [n]).
@@ -140,6 +157,9 @@ def attention_rows(q, k, v, rows, kv_len=None, threads=None, return_lse=False):
         lse.ctypes.data if lse is not None else None, threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle failed with {rc}")
+    if gate is not None:
+        g = _gate(gate, (B, Sq, H, D))
+        out *= g[rows[:, 0], rows[:, 2], rows[:, 1]]
     return (out, lse) if return_lse else out
 
 
@@ -158,12 +178,13 @@ def pairing(kind: str, inputs: dict, audio_kv_len: int):
     raise ValueError(kind)
 
 
-def block_attention(inputs: dict, audio_kv_len: int, kinds=KINDS, threads=None):
-    """All four attentions of one block; returns {kind: o float64 [B, Sq, H, D]}."""
+def block_attention(inputs: dict, audio_kv_len: int, kinds=KINDS, threads=None, gates=None):
+    """All four attentions of one block; returns {kind: o float64 [B, Sq, H, D]}.
+    gates: optional {kind: gate [B, Sq, H, D]}."""
     out = {}
     for kind in kinds:
         q, k, v, L = pairing(kind, inputs, audio_kv_len)
-        out[kind] = attention(q, k, v, kv_len=L, threads=threads)
+        out[kind] = attention(q, k, v, kv_len=L, threads=threads, gate=(gates or {}).get(kind))
     return out
 
 

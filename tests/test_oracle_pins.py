@@ -131,3 +131,57 @@ def test_bad_sizes_rejected():
         oracle.attention(z, z, z, kv_len=0)
     with pytest.raises(ValueError):
         oracle.attention(z, z, z, kv_len=5)
+
+
+# ---------------------------------------------------------------- output gate
+def _gate_case(seed=9):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((2, 7, 3, 8)).astype(np.float32)
+    k = rng.standard_normal((2, 11, 3, 8)).astype(np.float32)
+    v = rng.standard_normal((2, 11, 3, 8)).astype(np.float32)
+    return q, k, v
+
+
+def test_gate_closed_forms():
+    """All-ones leaves the output unchanged, all-zeros clears it, a gate of 2
+    doubles it exactly (a power of two), in every row and channel."""
+    q, k, v = _gate_case()
+    base = oracle.attention(q, k, v, kv_len=9)
+    shape = base.shape
+    assert np.array_equal(oracle.attention(q, k, v, kv_len=9, gate=np.ones(shape, np.float32)), base)
+    assert np.array_equal(oracle.attention(q, k, v, kv_len=9, gate=np.zeros(shape, np.float32)),
+                          np.zeros(shape))
+    assert np.array_equal(oracle.attention(q, k, v, kv_len=9, gate=np.full(shape, 2, np.float32)), 2 * base)
+
+
+def test_gate_follows_query_row_and_channel():
+    """A gate that is 1 on some (query row, head, channel) cells and 0 on the
+    others keeps exactly those cells of the ungated output; the rows entry
+    point applies the same cells."""
+    q, k, v = _gate_case(10)
+    base = oracle.attention(q, k, v, kv_len=11)
+    B, Sq, H, D = base.shape
+    b, i, h, d = np.meshgrid(*[np.arange(n) for n in (B, Sq, H, D)], indexing="ij")
+    gate = ((b + 2 * i + 3 * h + 5 * d) % 3 == 0).astype(np.float32)
+    got = oracle.attention(q, k, v, kv_len=11, gate=gate)
+    assert np.array_equal(got, np.where(gate == 1, base, 0.0))
+    rows = np.array([[0, 0, 0], [1, 2, 6], [0, 1, 3], [1, 0, 5]])
+    o = oracle.attention_rows(q, k, v, rows, kv_len=11, gate=gate)
+    for n, (bb, hh, ii) in enumerate(rows):
+        assert np.array_equal(o[n], got[bb, ii, hh])
+
+
+def test_gate_on_the_wrong_axis_is_caught():
+    """A mistaken reading that gates by key position instead of query row fails
+    the row pin above (so that pin can tell the two apart)."""
+    q, k, v = _gate_case(11)
+    base = oracle.attention(q, k, v, kv_len=11)
+    B, Sq, H, D = base.shape
+    gate = np.zeros((B, Sq, H, D), np.float32)
+    gate[:, 0] = 1.0                                   # keep query row 0 only
+    right = oracle.attention(q, k, v, kv_len=11, gate=gate)
+    # the mutant: weight the values of key 0 only (the same index, read as a key)
+    vm = np.zeros_like(v)
+    vm[:, 0] = v[:, 0]
+    wrong = oracle.attention(q, k, vm, kv_len=11)
+    assert np.array_equal(right[:, 0], base[:, 0]) and not np.allclose(wrong[:, 0], base[:, 0])
