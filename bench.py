@@ -133,6 +133,9 @@ def main():
     ap.add_argument("--distinct", action="store_true",
                     help="give every kind its own copies of its Q/K/V (no kind reads another's inputs "
                          "through the caches)")
+    ap.add_argument("--gated", action="store_true",
+                    help="gated attention: every kind's output multiplied by a gate of its shape "
+                         "(uniform in (0, 1), bf16)")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write this many MiB of scratch between block calls (past the last-level "
                          "cache); value then comes from the library's per-call events")
@@ -176,7 +179,11 @@ def main():
         pairs = {"video_self": ("video_q", "video_k", "video_v"), "audio_self": ("audio_q", "audio_k", "audio_v"),
                  "a2v": ("video_q", "audio_k", "audio_v"), "v2a": ("audio_q", "video_k", "video_v")}
         kind_inputs = {k: tuple(dev[n].clone() for n in names) for k, names in pairs.items()}
-    io = ba.make_io(dev, w.audio_kv_len, outs, kind_inputs)
+    gates = None
+    if args.gated:
+        gates = {k: (torch.rand_like(outs[k], dtype=torch.float32) * 0.999 + 0.0005).to(torch.bfloat16)
+                 for k in KINDS}
+    io = ba.make_io(dev, w.audio_kv_len, outs, kind_inputs, gates)
     scratch = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device="cuda:0")
                if args.flush_mib else None)
 
@@ -220,6 +227,10 @@ def main():
 
     flops = synth.attention_flops(w)
     nbytes = synth.attention_bytes(w)
+    if args.gated:   # the gate is read once, like the output is written once
+        qrows = {"video_self": w.video_len, "audio_self": w.audio_len, "a2v": w.video_len, "v2a": w.audio_len}
+        for k in KINDS:
+            nbytes[k] += 2 * w.batch * qrows[k] * w.heads * w.head_dim
     ms_step = wall * 1e3 / args.steps
     if scratch is not None:   # the flush is not the block's work: time the calls by their events
         ms_step = float(np.mean([r["total"] for r in rec]))
@@ -261,6 +272,7 @@ def main():
                    "audio_buffer_rows": w.audio_len, "parallelism": "none (1 GPU)",
                  "schedule": "overlap" if args.overlap else "sequential",
                  "inputs": "distinct per kind" if args.distinct else "two stream triples",
+                 "output_gate": bool(args.gated),
                  "flush_mib_between_calls": args.flush_mib},
         "kinds": kinds,
         "roofline": {"kernel": video_kernel_name(w),

@@ -93,8 +93,15 @@ typedef struct {
     int64_t stride_b, stride_s, stride_h;
 } ltxattn_tensor;
 
+/* One attention's tensors.  gate is optional (gate.data == NULL: none):
+ * a per-channel output gate of o's shape and layout rules, bf16; when given,
+ * o = gate * softmax(Q K^T / sqrt(D)) V elementwise, the product taken in
+ * fp32 before the output's rounding to bf16.  PR #1586 names gated attention
+ * among the DiT's parts without its formula: the gate values, already
+ * activated, come from the caller.  A gate may alias inputs, not outputs. */
 typedef struct {
     ltxattn_tensor q, k, v, o;
+    ltxattn_tensor gate;
 } ltxattn_attn_io;
 
 /* One block call.  Row counts by kind:
@@ -102,6 +109,7 @@ typedef struct {
  *   AUDIO_SELF: q, k, v, o have audio_len rows;
  *   A2V: q, o have video_len rows, k, v have audio_len rows;
  *   V2A: q, o have audio_len rows, k, v have video_len rows.
+ * gate, when given, has the rows of o.
  * Keys j >= audio_kv_len are masked whenever K/V are audio (AUDIO_SELF, A2V);
  * 1 <= audio_kv_len <= audio_len.  An entry with o.data == NULL is skipped.
  * The four entries may share input tensors (the usual case: one video and

@@ -188,10 +188,11 @@ def block_attention(inputs: dict, audio_kv_len: int, kinds=KINDS, threads=None, 
     return out
 
 
-def block_attention_rows(inputs: dict, audio_kv_len: int, rows: dict, threads=None):
-    """Selected rows of each attention: rows = {kind: int array [n, 3] of (b, h, i)}."""
+def block_attention_rows(inputs: dict, audio_kv_len: int, rows: dict, threads=None, gates=None):
+    """Selected rows of each attention: rows = {kind: int array [n, 3] of (b, h, i)};
+    gates: optional {kind: gate [B, Sq, H, D]}."""
     out = {}
     for kind, r in rows.items():
         q, k, v, L = pairing(kind, inputs, audio_kv_len)
-        out[kind] = attention_rows(q, k, v, r, kv_len=L, threads=threads)
+        out[kind] = attention_rows(q, k, v, r, kv_len=L, threads=threads, gate=(gates or {}).get(kind))
     return out

@@ -184,3 +184,43 @@ def test_huge_slice_unsupported():
                                                         big * 1024, 1024, 64))
     io.attn[1].o.data = io.attn[2].o.data = io.attn[3].o.data = None
     assert check(io, cfg) == lt.LTXATTN_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------ output gates
+def _gated_io():
+    """make_io() with a gate on every kind, each in a window of its own."""
+    io = make_io()
+    base, win = 1 << 40, 1 << 30
+    for k in range(4):
+        io.attn[k].gate = _t(base + (10 + k) * win, Sv if k in (0, 2) else La)
+    return io
+
+
+def test_gates_pass_and_may_alias_inputs():
+    assert check(_gated_io()) == lt.LTXATTN_OK
+    io = _gated_io()
+    io.attn[0].gate = io.attn[0].q          # a gate is an input: it may be any input tensor
+    io.attn[3].gate = io.attn[1].q
+    assert check(io) == lt.LTXATTN_OK
+
+
+@pytest.mark.parametrize("kind", range(4))
+def test_bad_gate(kind):
+    for mutate in ("misaligned", "stride_s_small", "stride_odd", "short", "overlaps_own_output",
+                   "overlaps_other_output"):
+        io = _gated_io()
+        g = io.attn[kind].gate
+        if mutate == "misaligned":
+            g.data = g.data + 8
+        elif mutate == "stride_s_small":
+            g.stride_s = D - 8
+        elif mutate == "stride_odd":
+            g.stride_s = ROW + 4
+        elif mutate == "short":                      # rows of this kind's output beyond 32-bit reach
+            g.stride_s = 1 << 24
+        elif mutate == "overlaps_own_output":
+            io.attn[kind].gate = io.attn[kind].o
+        else:
+            io.attn[kind].gate = io.attn[(kind + 1) % 4].o
+        want = lt.LTXATTN_ERR_UNSUPPORTED if mutate == "short" else lt.LTXATTN_ERR_INVALID_ARG
+        assert check(io) == want, (kind, mutate)

@@ -38,7 +38,7 @@ def test_bench_json_line():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("flag", ["--overlap", "--distinct"])
+@pytest.mark.parametrize("flag", ["--overlap", "--distinct", "--gated"])
 def test_bench_modes(flag):
     d = run_bench("--no-cpu-baseline", flag)
     assert d["value"] > 0 and "cpu_baseline" not in d

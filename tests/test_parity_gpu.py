@@ -36,12 +36,13 @@ def lt(torch):
     return ltxattn
 
 
-def run_block(lt, torch, w, inputs, kinds=KINDS):
+def run_block(lt, torch, w, inputs, kinds=KINDS, gates=None):
     log(f"  GPU block: {w.name} B{w.batch} H{w.heads} D{w.head_dim} Sv{w.video_len} "
-        f"La{w.audio_len} Lk{w.audio_kv_len} kinds={list(kinds)}")
+        f"La{w.audio_len} Lk{w.audio_kv_len} kinds={list(kinds)}{' gated' if gates else ''}")
     dev = {n: to_device(a) for n, a in inputs.items()}
+    dev_gates = {k: to_device(g) for k, g in gates.items()} if gates else None
     ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
-    outs = ba(dev, w.audio_kv_len, kinds=kinds)
+    outs = ba(dev, w.audio_kv_len, kinds=kinds, gates=dev_gates)
     torch.cuda.synchronize()
     res = {k: to_numpy(v) for k, v in outs.items()}
     ba.close()
@@ -277,6 +278,43 @@ def test_distinct_tensors_per_kind(lt, torch):
         want = oracle.attention(q, kk, vv, kv_len=w.audio_kv_len if kv_of[k] == "audio" else None)
         compare(to_numpy(outs[k]), want, f"distinct inputs {k}")
     ba.close()
+
+
+def make_gates(w, seed):
+    """A gate per kind, uniform in (0, 1) like an activated gate, bf16."""
+    rng = np.random.default_rng(seed)
+    rows = {"video_self": w.video_len, "audio_self": w.audio_len, "a2v": w.video_len, "v2a": w.audio_len}
+    return {k: synth.bf16_bits(rng.uniform(0, 1, (w.batch, rows[k], w.heads, w.head_dim)).astype(np.float32))
+            for k in KINDS}
+
+
+@pytest.mark.parametrize("w", [synth.WORKLOADS[1]] + [r for r in RAGGED if r.cfg in (11, 12, 17)],
+                         ids=lambda w: w.name)
+def test_gated_outputs(lt, torch, w):
+    """Gated attention (o = gate * attention, per channel) on every output path:
+    the two-buffer kernel at D = 128 and 64, the ring kernel, v2a and its
+    combine, the resident-key kernel with and without row staging."""
+    inputs = synth.make_block_inputs(w)
+    gates = make_gates(w, 100 + w.cfg)
+    got = run_block(lt, torch, w, inputs, gates=gates)
+    want = oracle.block_attention(inputs, w.audio_kv_len, gates=gates)
+    for k in KINDS:
+        compare(got[k], want[k], f"{w.name} gated {k}")
+
+
+def test_gated_split_tail(lt, torch):
+    """The gate on the split last-round items of video self-attention (applied
+    by the combine kernel), in the staggered dealing order."""
+    w, split_heads, (lo, hi) = TAIL_SPLITS[1]
+    inputs = synth.make_block_inputs(w)
+    gates = make_gates(w, 132)
+    got = run_block(lt, torch, w, inputs, kinds=("video_self",), gates={"video_self": gates["video_self"]})
+    rng = np.random.default_rng(7)
+    rows = np.array([(0, h, int(i)) for h in split_heads for i in list(rng.integers(lo, hi, 4)) + [lo, hi - 1]]
+                    + [(0, h, int(rng.integers(0, lo))) for h in range(w.heads)], np.int64)
+    want = oracle.block_attention_rows(inputs, w.audio_kv_len, {"video_self": rows},
+                                       gates={"video_self": gates["video_self"]})["video_self"]
+    compare(got["video_self"][rows[:, 0], rows[:, 2], rows[:, 1], :], want, "gated tail-split rows")
 
 
 def test_strided_layouts_and_guard_bands(lt, torch):

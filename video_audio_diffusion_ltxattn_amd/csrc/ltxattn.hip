@@ -99,6 +99,8 @@ struct FaArgs {
     int64_t v_sb, v_ss, v_sh;
     __bf16 *o;
     int64_t o_sb, o_ss, o_sh;
+    const __bf16 *g;  // output gate (null: none), o's shape
+    int64_t g_sb, g_ss, g_sh;
     float *part_o;    // split items: [split index][part][bm][D] fp32, unnormalised
     float *part_ml;   // split items: [split index][part][bm][2] = (row max * log2e/sqrt(D), row sum)
     int B, H, Sq, kv_len;
@@ -120,6 +122,8 @@ struct CombineArgs {
     const float *part_o, *part_ml;
     __bf16 *o;
     int64_t o_sb, o_ss, o_sh;
+    const __bf16 *g;
+    int64_t g_sb, g_ss, g_sh;
     int H, Sq, bm, n_qtiles, ipg, wpg, n_split_items, nsplit;
 };
 
@@ -190,6 +194,29 @@ constexpr float RESCALE_LOG2 = 8.0f;
 // The same bound on a lane's sum of probabilities in one tile: a sum at most
 // 2^RESCALE_LOG2 has every term at most 2^RESCALE_LOG2.
 constexpr float RESCALE_SUM = 256.0f;
+
+// One output row from its O^T fragments (o[db][i*4+j] = O^T[32db + 8i + 4hw + j]):
+// bf16(acc * inv), or bf16((acc * inv) * gate) with a gate row.
+template <int NDB>
+__device__ __forceinline__ void store_row(__bf16 *orow, const __bf16 *grow, bool gated, const f32x16 *o,
+                                          float inv, int hw) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int col = 32 * db + 8 * i + 4 * hw;
+            bf16x4 ov;
+            if (gated) {
+                const bf16x4 gv = *(const bf16x4 *)(grow + col);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ov[j] = (__bf16)((o[db][i * 4 + j] * inv) * (float)gv[j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(o[db][i * 4 + j] * inv);
+            }
+            *(bf16x4 *)(orow + col) = ov;
+        }
+}
 
 template <int D>
 struct RowState {
@@ -458,19 +485,10 @@ void fa_fwd_kernel(const FaArgs a) {
     // st.o[db][i*4+j] is O^T[d = 32db + 8i + 4hw + j][query qrow] (unnormalised).
     const float l_tot = xhalf_sum(st.l);
     if (!split_item) {
-        if (qrow < a.Sq) {
-            const float inv = 1.0f / l_tot;
-            __bf16 *orow = a.o + b * a.o_sb + (int64_t)qrow * a.o_ss + hh * a.o_sh;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    bf16x4 ov;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(st.o[db][i * 4 + j] * inv);
-                    *(bf16x4 *)(orow + 32 * db + 8 * i + 4 * hw) = ov;
-                }
-        }
+        if (qrow < a.Sq)
+            store_row<NDB>(a.o + b * a.o_sb + (int64_t)qrow * a.o_ss + hh * a.o_sh,
+                           a.g + b * a.g_sb + (int64_t)qrow * a.g_ss + hh * a.g_sh, a.g != nullptr,
+                           st.o, 1.0f / l_tot, hw);
     } else {
         const int64_t prow = ((int64_t)split_idx * a.nsplit + part) * BM + (qrow - qt * BM);
         float *po = a.part_o + prow * D;
@@ -862,19 +880,10 @@ void fa_ring_kernel(const FaArgs a) {
 
     // st.o[db][i*4+j] is O^T[d = 32db + 8i + 4hw + j][query qrow] (unnormalised).
     if (!split_item) {
-        if (qrow < a.Sq) {
-            const float inv = 1.0f / l_tot;
-            __bf16 *orow = a.o + b * a.o_sb + (int64_t)qrow * a.o_ss + hh * a.o_sh;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    bf16x4 ov;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(st.o[db][i * 4 + j] * inv);
-                    *(bf16x4 *)(orow + 32 * db + 8 * i + 4 * hw) = ov;
-                }
-        }
+        if (qrow < a.Sq)
+            store_row<NDB>(a.o + b * a.o_sb + (int64_t)qrow * a.o_ss + hh * a.o_sh,
+                           a.g + b * a.g_sb + (int64_t)qrow * a.g_ss + hh * a.g_sh, a.g != nullptr,
+                           st.o, 1.0f / l_tot, hw);
     } else {
         const int64_t prow = ((int64_t)split_idx * a.nsplit + part) * BM + (qrow - qt * BM);
         float *po = a.part_o + prow * D;
@@ -909,7 +918,7 @@ void fa_ring_kernel(const FaArgs a) {
 // No workgroup barrier is needed except when the head changes.
 constexpr int KVRES_SLOT = 32 * 128 * 2;   // one wave's 32 rows of Q or O at D = 128 (8 KB)
 
-template <int D, int NW, bool STAGED>
+template <int D, int NW, bool STAGED, bool GATED>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2)))
 void fa_kvres_kernel(const FaArgs a) {
     constexpr int BM = 32 * NW, KS = D / 16, NDB = D / 32, NKB = BN / 32, PS = BN / 16;
@@ -968,18 +977,22 @@ void fa_kvres_kernel(const FaArgs a) {
         return make_rsrc(a.q + b * a.q_sb + hh * a.q_sh, ((int64_t)(a.Sq - 1) * a.q_ss + D) * 2);
     };
     auto q_row0 = [&](int item) { return (item % a.n_qtiles) * BM + wave * 32; };
-    auto dma_q = [&](int item, LDS_AS char *slot) {
-        const __amdgpu_buffer_rsrc_t qr = q_rsrc(item);
+    // 32 rows of this wave's query tile from a [B, Sq, H, D] tensor (Q, or
+    // the output gate) into a slot.
+    auto dma_rows = [&](int item, LDS_AS char *slot, const __bf16 *t, int64_t sb, int64_t ss, int64_t sh) {
+        const int bh = item / a.n_qtiles, b = bh / a.H, hh = bh % a.H;
+        const __amdgpu_buffer_rsrc_t tr = make_rsrc(t + b * sb + hh * sh, ((int64_t)(a.Sq - 1) * ss + D) * 2);
         const int r0 = q_row0(item);
 #pragma unroll
         for (int n = 0; n < 32 * (D / 8) / 64; ++n) {
             const int idx = n * 64 + lane;              // physical chunk in the slot
             const int r = idx / (D / 8), p = idx % (D / 8);
             const int c = swz_k<D>(r, p);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (LDS_AS void *)(slot + n * 1024), 16,
-                                                     (int)((int64_t)(r0 + r) * a.q_ss * 2) + c * 16, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(tr, (LDS_AS void *)(slot + n * 1024), 16,
+                                                     (int)((int64_t)(r0 + r) * ss * 2) + c * 16, 0, 0, 0);
         }
     };
+    auto dma_q = [&](int item, LDS_AS char *slot) { dma_rows(item, slot, a.q, a.q_sb, a.q_ss, a.q_sh); };
     auto regs_q = [&](int item, bf16x8 *qf) {
         const __amdgpu_buffer_rsrc_t qr = q_rsrc(item);
         const int qrow = q_row0(item) + l32;
@@ -1015,6 +1028,10 @@ void fa_kvres_kernel(const FaArgs a) {
             for (int k = 0; k < KS; ++k)
                 qf[k] = __builtin_bit_cast(bf16x8,
                     *(const LDS_AS u32x4 *)(slot + l32 * ROWB + swz_k<D>(l32, 2 * k + hw) * 16));
+            if constexpr (GATED) {   // the gate rows of this tile take Q's place in the slot
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                dma_rows(item, slot, a.g, a.g_sb, a.g_ss, a.g_sh);
+            }
         } else if (item + 1 < i_end) {
             regs_q(item + 1, qn);
         }
@@ -1041,15 +1058,25 @@ void fa_kvres_kernel(const FaArgs a) {
         if (STAGED) {
             // O^T fragments -> row-major rows in `slot` (its Q is in registers
             // already), then whole rows out with 16 bytes per lane.
+            // Gated: the slot holds the gate rows (loaded during the compute);
+            // each lane reads its gate values where its output values go.
+            if constexpr (GATED) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    bf16x4 ov;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(st.o[db][i * 4 + j] * inv);
                     const int col = 32 * db + 8 * i + 4 * hw;   // element column of ov[0]
-                    *(LDS_AS bf16x4 *)(slot + l32 * ROWB + swz_k<D>(l32, col >> 3) * 16 + (col & 7) * 2) = ov;
+                    LDS_AS bf16x4 *cell = (LDS_AS bf16x4 *)(slot + l32 * ROWB + swz_k<D>(l32, col >> 3) * 16 + (col & 7) * 2);
+                    bf16x4 ov;
+                    if constexpr (GATED) {
+                        const bf16x4 gv = *cell;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) ov[j] = (__bf16)((st.o[db][i * 4 + j] * inv) * (float)gv[j]);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(st.o[db][i * 4 + j] * inv);
+                    }
+                    *cell = ov;
                 }
 #pragma unroll
             for (int n = 0; n < 32 * (D / 8) / 64; ++n) {
@@ -1065,18 +1092,10 @@ void fa_kvres_kernel(const FaArgs a) {
             }
         } else {
             const int qrow = qrow0 + l32;
-            if (qrow < a.Sq) {
-                __bf16 *orow = obase + (int64_t)qrow * a.o_ss;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        bf16x4 ov;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) ov[j] = (__bf16)(st.o[db][i * 4 + j] * inv);
-                        *(bf16x4 *)(orow + 32 * db + 8 * i + 4 * hw) = ov;
-                    }
-            }
+            if (qrow < a.Sq)
+                store_row<NDB>(obase + (int64_t)qrow * a.o_ss,
+                               a.g + b * a.g_sb + (int64_t)qrow * a.g_ss + hh * a.g_sh, GATED,
+                               st.o, inv, hw);
 #pragma unroll
             for (int k = 0; k < KS; ++k) qf[k] = qn[k];
         }
@@ -1115,8 +1134,14 @@ void fa_combine_kernel(const CombineArgs a) {
     }
     const float inv = 1.0f / L;
     bf16x4 out;
+    if (a.g) {
+        const bf16x4 gv = *(const bf16x4 *)(a.g + b * a.g_sb + (int64_t)q * a.g_ss + hh * a.g_sh + d4 * 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = (__bf16)(acc[j] * inv);
+        for (int j = 0; j < 4; ++j) out[j] = (__bf16)((acc[j] * inv) * (float)gv[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = (__bf16)(acc[j] * inv);
+    }
     *(bf16x4 *)(a.o + b * a.o_sb + (int64_t)q * a.o_ss + hh * a.o_sh + d4 * 4) = out;
 }
 
@@ -1219,6 +1244,8 @@ int run_resident_kv(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq,
     a.v_sb = io.v.stride_b; a.v_ss = io.v.stride_s; a.v_sh = io.v.stride_h;
     a.o = (__bf16 *)io.o.data;
     a.o_sb = io.o.stride_b; a.o_ss = io.o.stride_s; a.o_sh = io.o.stride_h;
+    a.g = (const __bf16 *)io.gate.data;
+    a.g_sb = io.gate.stride_b; a.g_ss = io.gate.stride_s; a.g_sh = io.gate.stride_h;
     a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const int nkt = ceil_div(kv_len, BN);
@@ -1239,12 +1266,21 @@ int run_resident_kv(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq,
     a.ipg = items / a.groups;
     const int per_group = std::min(a.ipg, (nw == 8 ? 1 : per_cu) * h->num_cus / a.groups);
     a.total = a.groups * per_group;
-    if (D == 128 && staged)
-        hipLaunchKernelGGL((fa_kvres_kernel<128, 8, true>), dim3(a.total), dim3(512), lds, st, a);
+    // Gated outputs take instantiations of their own, so that the ungated
+    // ones are compiled without any gate code.
+    if (a.g) {
+        if (D == 128 && staged)
+            hipLaunchKernelGGL((fa_kvres_kernel<128, 8, true, true>), dim3(a.total), dim3(512), lds, st, a);
+        else if (D == 128 && nw == 8)
+            hipLaunchKernelGGL((fa_kvres_kernel<128, 8, false, true>), dim3(a.total), dim3(512), lds, st, a);
+        else if (D == 128) hipLaunchKernelGGL((fa_kvres_kernel<128, 4, false, true>), dim3(a.total), dim3(256), lds, st, a);
+        else hipLaunchKernelGGL((fa_kvres_kernel<64, 4, false, true>), dim3(a.total), dim3(256), lds, st, a);
+    } else if (D == 128 && staged)
+        hipLaunchKernelGGL((fa_kvres_kernel<128, 8, true, false>), dim3(a.total), dim3(512), lds, st, a);
     else if (D == 128 && nw == 8)
-        hipLaunchKernelGGL((fa_kvres_kernel<128, 8, false>), dim3(a.total), dim3(512), lds, st, a);
-    else if (D == 128) hipLaunchKernelGGL((fa_kvres_kernel<128, 4, false>), dim3(a.total), dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((fa_kvres_kernel<64, 4, false>), dim3(a.total), dim3(256), lds, st, a);
+        hipLaunchKernelGGL((fa_kvres_kernel<128, 8, false, false>), dim3(a.total), dim3(512), lds, st, a);
+    else if (D == 128) hipLaunchKernelGGL((fa_kvres_kernel<128, 4, false, false>), dim3(a.total), dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((fa_kvres_kernel<64, 4, false, false>), dim3(a.total), dim3(256), lds, st, a);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? LTXATTN_OK : hip_fail(h, e);
 }
@@ -1254,6 +1290,7 @@ int run_combine(ltxattn_handle *h, const FaArgs &a, int bm, int n_split_items, h
     CombineArgs c;
     c.part_o = a.part_o; c.part_ml = a.part_ml;
     c.o = a.o; c.o_sb = a.o_sb; c.o_ss = a.o_ss; c.o_sh = a.o_sh;
+    c.g = a.g; c.g_sb = a.g_sb; c.g_ss = a.g_ss; c.g_sh = a.g_sh;
     c.H = a.H; c.Sq = a.Sq; c.bm = bm; c.n_qtiles = a.n_qtiles; c.ipg = a.ipg; c.wpg = a.wpg;
     c.n_split_items = n_split_items; c.nsplit = a.nsplit;
     const int64_t threads = (int64_t)n_split_items * bm * (h->head_dim / 4);
@@ -1278,6 +1315,8 @@ int run_stream(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int 
     a.v_sb = io.v.stride_b; a.v_ss = io.v.stride_s; a.v_sh = io.v.stride_h;
     a.o = (__bf16 *)io.o.data;
     a.o_sb = io.o.stride_b; a.o_ss = io.o.stride_s; a.o_sh = io.o.stride_h;
+    a.g = (const __bf16 *)io.gate.data;
+    a.g_sb = io.gate.stride_b; a.g_ss = io.gate.stride_s; a.g_sh = io.gate.stride_h;
     a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
     a.n_qtiles = ceil_div(Sq, BM);
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
@@ -1334,6 +1373,8 @@ int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, i
     a.v_sb = io.v.stride_b; a.v_ss = io.v.stride_s; a.v_sh = io.v.stride_h;
     a.o = (__bf16 *)io.o.data;
     a.o_sb = io.o.stride_b; a.o_ss = io.o.stride_s; a.o_sh = io.o.stride_h;
+    a.g = (const __bf16 *)io.gate.data;
+    a.g_sb = io.gate.stride_b; a.g_ss = io.gate.stride_s; a.g_sh = io.gate.stride_h;
     a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
     a.n_qtiles = ceil_div(Sq, BM);
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
@@ -1405,7 +1446,7 @@ int validate_block(const ltxattn_config &caps, const ltxattn_block_io *io, bool 
     // Rows of q/o and of k/v per kind.
     const int q_rows[4] = {Sv, La, Sv, La};
     const int kv_rows[4] = {Sv, La, La, Sv};
-    Extent in_ext[4][3], out_ext[4];
+    Extent in_ext[4][4] = {}, out_ext[4];
     for (int k = 0; k < 4; ++k) {
         const ltxattn_attn_io &x = io->attn[k];
         on[k] = x.o.data != nullptr;
@@ -1415,12 +1456,13 @@ int validate_block(const ltxattn_config &caps, const ltxattn_block_io *io, bool 
         if ((rc = check_tensor(x.k, B, kv_rows[k], H, D, &in_ext[k][1]))) return rc;
         if ((rc = check_tensor(x.v, B, kv_rows[k], H, D, &in_ext[k][2]))) return rc;
         if ((rc = check_tensor(x.o, B, q_rows[k], H, D, &out_ext[k]))) return rc;
+        if (x.gate.data && (rc = check_tensor(x.gate, B, q_rows[k], H, D, &in_ext[k][3]))) return rc;
     }
     for (int k = 0; k < 4; ++k) {
         if (!on[k]) continue;
         for (int j = 0; j < 4; ++j) {
             if (!on[j]) continue;
-            for (int t = 0; t < 3; ++t)
+            for (int t = 0; t < 4; ++t)   // q, k, v, gate (an absent gate spans nothing)
                 if (overlaps(out_ext[k], in_ext[j][t])) return LTXATTN_ERR_INVALID_ARG;
             if (j != k && overlaps(out_ext[k], out_ext[j])) return LTXATTN_ERR_INVALID_ARG;
         }
@@ -1572,17 +1614,15 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
     if (e != hipSuccess) { g_create_hip_error = (int)e; free(h); return LTXATTN_ERR_HIP; }
     // The resident-key kernel keeps up to RESIDENT_KV_MAX keys of K and V (and,
     // staged, the Q/O row slots) in LDS: allow it all of a CU's LDS.
-    e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<128, 8, true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<128, 8, false>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<128, 4, false>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_kvres_kernel<64, 4, false>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+    {
+        const void *kvres[8] = {
+            (const void *)&fa_kvres_kernel<128, 8, true, false>, (const void *)&fa_kvres_kernel<128, 8, true, true>,
+            (const void *)&fa_kvres_kernel<128, 8, false, false>, (const void *)&fa_kvres_kernel<128, 8, false, true>,
+            (const void *)&fa_kvres_kernel<128, 4, false, false>, (const void *)&fa_kvres_kernel<128, 4, false, true>,
+            (const void *)&fa_kvres_kernel<64, 4, false, false>, (const void *)&fa_kvres_kernel<64, 4, false, true>};
+        for (int i = 0; i < 8 && e == hipSuccess; ++i)
+            e = hipFuncSetAttribute(kvres[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+    }
     if (e == hipSuccess)
         e = hipFuncSetAttribute((const void *)&fa_ring_kernel<128, RING_NW, 2>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 128 * 2);

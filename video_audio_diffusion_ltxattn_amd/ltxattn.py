@@ -52,7 +52,8 @@ class ltxattn_tensor(ctypes.Structure):
 
 class ltxattn_attn_io(ctypes.Structure):
     _fields_ = [("q", ltxattn_tensor), ("k", ltxattn_tensor),
-                ("v", ltxattn_tensor), ("o", ltxattn_tensor)]
+                ("v", ltxattn_tensor), ("o", ltxattn_tensor),
+                ("gate", ltxattn_tensor)]   # gate.data = None: no output gate
 
 
 class ltxattn_block_io(ctypes.Structure):
@@ -227,9 +228,11 @@ class BlockAttention:
         except Exception:
             pass
 
-    def make_io(self, streams: dict, audio_kv_len: int, outs: dict, inputs: dict = None) -> ltxattn_block_io:
+    def make_io(self, streams: dict, audio_kv_len: int, outs: dict, inputs: dict = None,
+                gates: dict = None) -> ltxattn_block_io:
         """streams: video_q/k/v, audio_q/k/v tensors; outs: {kind name: output tensor};
-        inputs: optional {kind name: (q, k, v)} replacing that kind's stream tensors.
+        inputs: optional {kind name: (q, k, v)} replacing that kind's stream tensors;
+        gates: optional {kind name: gate tensor of that output's shape}.
         The struct holds raw device pointers: every tensor named here must stay
         alive until the work enqueued with it has completed."""
         vq, vk, vv = streams["video_q"], streams["video_k"], streams["video_v"]
@@ -242,17 +245,19 @@ class BlockAttention:
         pairs.update(inputs or {})
         for name, o in outs.items():
             q, k, v = pairs[name]
-            io.attn[KIND_INDEX[name]] = ltxattn_attn_io(tensor_desc(q), tensor_desc(k),
-                                                        tensor_desc(v), tensor_desc(o))
+            g = (gates or {}).get(name)
+            io.attn[KIND_INDEX[name]] = ltxattn_attn_io(tensor_desc(q), tensor_desc(k), tensor_desc(v),
+                                                        tensor_desc(o),
+                                                        tensor_desc(g) if g is not None else ltxattn_tensor())
         return io
 
     def __call__(self, streams: dict, audio_kv_len: int, kinds=KIND_NAMES, outs: dict = None,
-                 stream=None, overlap: bool = False) -> dict:
+                 stream=None, overlap: bool = False, gates: dict = None) -> dict:
         import torch
         if outs is None:
             vq, aq = streams["video_q"], streams["audio_q"]
             outs = {k: torch.empty_like(vq if k in ("video_self", "a2v") else aq) for k in kinds}
-        io = self.make_io(streams, audio_kv_len, outs)
+        io = self.make_io(streams, audio_kv_len, outs, gates=gates)
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
         call = ltxattn_block_attention_overlap if overlap else ltxattn_block_attention
         call(self.handle, io, s.cuda_stream)
