@@ -224,3 +224,35 @@ def test_bad_gate(kind):
             io.attn[kind].gate = io.attn[(kind + 1) % 4].o
         want = lt.LTXATTN_ERR_UNSUPPORTED if mutate == "short" else lt.LTXATTN_ERR_INVALID_ARG
         assert check(io) == want, (kind, mutate)
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The binding's ctypes structs have the C header's sizes and field offsets
+    (a C program built against include/ltxattn.h prints them)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    fields = {"ltxattn_config": [f for f, _ in lt.ltxattn_config._fields_],
+              "ltxattn_tensor": [f for f, _ in lt.ltxattn_tensor._fields_],
+              "ltxattn_attn_io": [f for f, _ in lt.ltxattn_attn_io._fields_],
+              "ltxattn_block_io": [f for f, _ in lt.ltxattn_block_io._fields_]}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "ltxattn.h"', "int main(void) {"]
+    for st, fs in fields.items():
+        lines.append(f'  printf("{st} %zu\\n", sizeof({st}));')
+        for f in fs:
+            lines.append(f'  printf("{st}.{f} %zu\\n", offsetof({st}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(root, "include"), "-o", str(exe), str(src)], check=True)
+    got = dict(ln.split() for ln in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                     check=True).stdout.splitlines())
+    for st, fs in fields.items():
+        cls = getattr(lt, st)
+        assert int(got[st]) == ctypes.sizeof(cls), st
+        for f in fs:
+            assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
