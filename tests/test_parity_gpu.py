@@ -442,9 +442,13 @@ def test_overlap_matches_sequential(lt, torch, cfg):
     log(f"  overlap vs sequential: {w.name}")
     seq = ba(dev, w.audio_kv_len)
     ovl = ba(dev, w.audio_kv_len, overlap=True)
+    gates = {k: to_device(g) for k, g in make_gates(w, 200 + cfg).items()}
+    seq_g = ba(dev, w.audio_kv_len, gates=gates)
+    ovl_g = ba(dev, w.audio_kv_len, overlap=True, gates=gates)
     torch.cuda.synchronize()
     for k in KINDS:
         assert torch.equal(seq[k].view(torch.int16), ovl[k].view(torch.int16)), k
+        assert torch.equal(seq_g[k].view(torch.int16), ovl_g[k].view(torch.int16)), k
     ba.close()
 
 
