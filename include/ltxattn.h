@@ -55,7 +55,8 @@ extern "C" {
 #define LTXATTN_ERR_INVALID_ARG (-1) /* null/misaligned pointer, bad stride, size out of range,
                                         output overlapping another tensor */
 #define LTXATTN_ERR_UNSUPPORTED (-2) /* head_dim not 64 or 128, heads < 1, tensor too large
-                                        for 32-bit buffer offsets */
+                                        for 32-bit buffer offsets, split parts that would not
+                                        fit the workspace */
 #define LTXATTN_ERR_HIP         (-3) /* a HIP call or kernel launch failed; see
                                         ltxattn_last_hip_error */
 #define LTXATTN_ERR_OOM         (-4) /* device workspace allocation failed */
@@ -72,10 +73,11 @@ enum {
 typedef struct ltxattn_handle ltxattn_handle;
 
 /* Fixed at create time.  heads and head_dim are shared by all four
- * attentions.  The max_* capacities bound every later call and size the
+ * attentions.  The max_* capacities bound every later call.  The handle's
  * device workspace of split work items (the key-range parts of v2a and of
- * an incomplete last round of video self-attention, in separate regions;
- * about 100 MB at 32 heads of 128 on a 256-CU device). */
+ * an incomplete last round of video self-attention, in separate regions)
+ * is sized by the device's compute units: 384 rows of head_dim + 2 floats
+ * per CU, 51 MB at head_dim 128 on a 256-CU MI355X. */
 typedef struct {
     int32_t device;        /* HIP device ordinal the handle and its kernels use */
     int32_t heads;         /* H >= 1 */
@@ -87,7 +89,8 @@ typedef struct {
 
 /* One bf16 tensor [B, S, H, D], D contiguous.  data is a device pointer,
  * 16-byte aligned; strides are in elements and must be multiples of 8 with
- * stride_s >= D and stride_h >= D.  Caller-owned. */
+ * stride_s >= D and stride_h >= D.  An output's distinct (b, s, h) rows must
+ * not share memory (inputs may, e.g. a batch stride of 0).  Caller-owned. */
 typedef struct {
     void *data;
     int64_t stride_b, stride_s, stride_h;
@@ -136,7 +139,9 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out);
  * them by log-sum-exp in a fixed order (VIDEO_SELF does the same for the
  * query tiles of an incomplete last round, when there is one); the other
  * work writes bf16 O directly.  Results are bit-identical from run to run.
- * Errors: INVALID_ARG, UNSUPPORTED (checked before any launch), HIP. */
+ * Every argument is checked, and every kind's launch and workspace planned,
+ * before anything is enqueued.
+ * Errors: INVALID_ARG, UNSUPPORTED (both before any launch), HIP. */
 int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void *hip_stream);
 
 /* The same block call with the audio side running beside video
@@ -146,9 +151,9 @@ int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void 
  * (HIP events; no host synchronisation).  Work enqueued on hip_stream after
  * the call therefore sees all four outputs, and the call can be captured
  * into a HIP graph from hip_stream.  Outputs are bit-identical to
- * ltxattn_block_attention's (the same kernels; the two sides use separate
- * workspace regions).  Calls on one handle must not overlap each other,
- * as for ltxattn_block_attention.  The audio side is a few percent of a
+ * ltxattn_block_attention's (the same kernels; only video self-attention
+ * and v2a use the workspace, each its own region).  Calls on one handle
+ * must not overlap each other, as for ltxattn_block_attention.  The audio side is a few percent of a
  * block (PR #16228, "Description"); whether running it beside video
  * self-attention shortens the block depends on how much of the device the
  * video kernel leaves free.
@@ -156,10 +161,11 @@ int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void 
 int ltxattn_block_attention_overlap(ltxattn_handle *h, const ltxattn_block_io *io, void *hip_stream);
 
 /* Validate a block call against a configuration without touching any
- * device: returns exactly the status ltxattn_block_attention would return
- * from its argument checks (LTXATTN_OK if the call would be launched).
- * Lets a caller check a request up front, and the checks be tested on a
- * machine without a GPU. */
+ * device: returns the status ltxattn_block_attention would return from its
+ * checks on a 256-CU MI355X (LTXATTN_OK if the call would be launched): the
+ * arguments, then the workspace each kind's split parts need against the
+ * handle's regions.  Lets a caller check a request up front, and the checks
+ * be tested on a machine without a GPU. */
 int ltxattn_check_block(const ltxattn_config *cfg, const ltxattn_block_io *io);
 
 /* Free the workspace and the handle.  The caller must make sure no work

@@ -256,3 +256,75 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert int(got[st]) == ctypes.sizeof(cls), st
         for f in fs:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
+
+
+# ------------------------------------------------- outputs with shared rows
+@pytest.mark.parametrize("case", ["s_and_h_same_stride", "batch_stride_zero", "h_inside_s_span",
+                                  "s_inside_b_span"])
+def test_output_rows_sharing_memory_rejected(case):
+    """Distinct (b, s, h) rows of an output must not share bytes; the same
+    strides on an input are accepted (a kernel only reads them)."""
+    for kind in range(4):
+        S = Sv if kind in (0, 2) else La
+        io = make_io()
+        o = io.attn[kind].o
+        if case == "s_and_h_same_stride":
+            o.stride_s, o.stride_h = D, D
+        elif case == "batch_stride_zero":
+            o.stride_b = 0
+        elif case == "h_inside_s_span":            # head-major, heads closer than S rows apart
+            o.stride_s, o.stride_h, o.stride_b = D, (S - 1) * D, S * ROW
+        else:                                      # batches closer than one batch's span
+            o.stride_b = S * ROW - D
+        io.attn[kind].o = o
+        assert check(io) == lt.LTXATTN_ERR_INVALID_ARG, (case, kind)
+        io = make_io()
+        q = io.attn[kind].q
+        q.stride_b, q.stride_s, q.stride_h = o.stride_b, o.stride_s, o.stride_h
+        io.attn[kind].q = q
+        assert check(io) == lt.LTXATTN_OK, (case, kind)
+
+
+def test_output_dims_of_extent_one_take_any_stride():
+    """A dimension of extent 1 spans nothing: its stride does not matter."""
+    cfg = lt.ltxattn_config(0, 1, D, 1, Sv, La)
+    io = make_io(batch=1)
+    for k in range(4):
+        for which in "qkvo":
+            t = getattr(io.attn[k], which)
+            t.stride_h = D                          # one head: the head stride is never used
+            t.stride_s = ROW
+            setattr(io.attn[k], which, t)
+    assert check(io, cfg) == lt.LTXATTN_OK
+
+
+# ------------------------------------------------ workspace of split parts
+def test_split_parts_fit_the_workspace_at_any_size():
+    """ltxattn_check_block also plans every kind for a 256-CU device and checks
+    the rows its split parts need (video self-attention's incomplete last
+    round, v2a's key ranges) against the workspace a handle has: over a sweep
+    of shapes up to and past the headline sizes, every request fits."""
+    import numpy as np
+    rng = np.random.default_rng(5)
+    shapes = [(1, 32, 128, 15360, 128, 126), (2, 32, 128, 15360, 128, 126), (1, 32, 128, 27280, 256, 252),
+              (1, 32, 128, 3840, 126, 126), (1, 8, 128, 9216, 640, 600), (1, 2, 128, 4096, 128, 128),
+              (1, 1, 128, 1281, 64, 64), (4, 48, 128, 40000, 1024, 1000), (1, 256, 64, 5000, 8, 8)]
+    for _ in range(60):
+        D_ = int(rng.choice([64, 128]))
+        La_ = int(rng.integers(1, 1200))
+        shapes.append((int(rng.integers(1, 5)), int(rng.integers(1, 65)), D_, int(rng.integers(1, 40001)),
+                       La_, int(rng.integers(1, La_ + 1))))
+    base, win = 1 << 44, 1 << 38
+    for B_, H_, D_, Sv_, La_, Lk_ in shapes:
+        row = H_ * D_
+        def t(i, S):
+            return lt.ltxattn_tensor(base + i * win, S * row, row, D_)
+        io = lt.ltxattn_block_io()
+        io.batch, io.video_len, io.audio_len, io.audio_kv_len = B_, Sv_, La_, Lk_
+        vq, vk, vv, aq, ak, av = t(0, Sv_), t(1, Sv_), t(2, Sv_), t(3, La_), t(4, La_), t(5, La_)
+        io.attn[0] = lt.ltxattn_attn_io(vq, vk, vv, t(6, Sv_))
+        io.attn[1] = lt.ltxattn_attn_io(aq, ak, av, t(7, La_))
+        io.attn[2] = lt.ltxattn_attn_io(vq, ak, av, t(8, Sv_))
+        io.attn[3] = lt.ltxattn_attn_io(aq, vk, vv, t(9, La_))
+        cfg = lt.ltxattn_config(0, H_, D_, B_, Sv_, La_)
+        assert lt.ltxattn_check_block(cfg, io) == lt.LTXATTN_OK, (B_, H_, D_, Sv_, La_, Lk_)

@@ -91,20 +91,52 @@ def sample_rows(rng, B, H, Sq, n_random=24):
     return np.array(rows, dtype=np.int64)
 
 
+def item_rows(rng, B, H, Sq, tile, per_tile=1):
+    """per_tile random rows of every (b, h, query tile of `tile` rows), plus the
+    first and last row of every (b, h): every work item of a kind whose items are
+    whole tiles of `tile` rows (or a multiple of it) has rows among them, its
+    split parts included (a split item's rows are finished from all its parts)."""
+    rows = []
+    for b in range(B):
+        for h in range(H):
+            rows += [(b, h, 0), (b, h, Sq - 1)]
+            for t0 in range(0, Sq, tile):
+                hi = min(Sq, t0 + tile)
+                rows += [(b, h, int(i)) for i in rng.integers(t0, hi, per_tile)]
+    return np.array(rows, dtype=np.int64)
+
+
+def block_item_rows(rng, w, video_tile=256, audio_tile=128, audio_per_tile=4):
+    """Rows covering every work item of every kind: video-query kinds (video self,
+    a2v) run 256-query items at these sizes (or 128), audio-query kinds 128."""
+    return {k: (item_rows(rng, w.batch, w.heads, w.video_len, video_tile)
+                if k in ("video_self", "a2v") else
+                item_rows(rng, w.batch, w.heads, w.audio_len, audio_tile, audio_per_tile))
+            for k in KINDS}
+
+
+def check_rows(got, want_rows, rows, what):
+    for k in want_rows:
+        r = rows[k]
+        compare(got[k][r[:, 0], r[:, 2], r[:, 1], :], want_rows[k], f"{what} {k}")
+
+
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_full_size_sampled(lt, torch, cfg):
+    """The full-size workloads: one oracle row from every work item of every
+    kind (every (b, h, query tile), split last-round items and v2a included),
+    fixed rows at tile edges, and properties of every row."""
     w = synth.WORKLOADS[cfg]
     inputs = synth.make_block_inputs(w)
     got = run_block(lt, torch, w, inputs)
     rng = np.random.default_rng(100 + cfg)
-    rows = {k: sample_rows(rng, w.batch, w.heads,
-                           w.video_len if k in ("video_self", "a2v") else w.audio_len,
-                           n_random=96 if k == "video_self" else 24)
-            for k in KINDS}
-    want = oracle.block_attention_rows(inputs, w.audio_kv_len, rows)
+    rows = block_item_rows(rng, w)
     for k in KINDS:
-        r = rows[k]
-        compare(got[k][r[:, 0], r[:, 2], r[:, 1], :], want[k], f"cfg{cfg} {k} sampled")
+        Sq = w.video_len if k in ("video_self", "a2v") else w.audio_len
+        rows[k] = np.concatenate([rows[k], sample_rows(rng, w.batch, w.heads, Sq, n_random=0)])
+    log(f"  oracle rows: " + ", ".join(f"{k} {len(r)}" for k, r in rows.items()))
+    want = oracle.block_attention_rows(inputs, w.audio_kv_len, rows)
+    check_rows(got, want, rows, f"cfg{cfg} every item")
     # every row: finite and inside the hull of the valid V rows of its (b, h)
     vv = synth.bits_to_f32(inputs["video_v"])
     av = synth.bits_to_f32(inputs["audio_v"])[:, :w.audio_kv_len]
@@ -115,6 +147,81 @@ def test_full_size_sampled(lt, torch, cfg):
         hi = bound[k].max(axis=1, keepdims=True) + 2e-2
         lo = bound[k].min(axis=1, keepdims=True) - 2e-2
         assert np.all(o <= hi) and np.all(o >= lo), f"cfg{cfg} {k}: output outside hull of valid V"
+
+
+# Blocks that reach launch configurations the workloads above do not, each
+# compared with the full oracle (every element):
+EDGE_BLOCKS = [
+    # v2a at its most parts: 2 items of 128 audio queries on 256 CUs -> 16
+    # parts of 256 video keys
+    synth.Workload(51, "v2a at 16 parts", 1, 2, 128, 4096, 128, 128),
+    # v2a in 5 parts of 320 keys whose last holds one key: its second key group
+    # sees no valid key at all (m stays at its start, merge weight 0); video
+    # self-attention with one valid row in its last query tile and one valid
+    # key in its last key tile
+    synth.Workload(52, "v2a one-key last part", 1, 1, 128, 1281, 64, 60),
+]
+
+
+@pytest.mark.parametrize("w", EDGE_BLOCKS, ids=lambda w: w.name)
+def test_edge_blocks_full_oracle(lt, torch, w):
+    inputs = synth.make_block_inputs(w)
+    got = run_block(lt, torch, w, inputs)
+    want = oracle.block_attention(inputs, w.audio_kv_len)
+    for k in KINDS:
+        compare(got[k], want[k], f"{w.name} {k}")
+
+
+# 200 valid audio keys of 256 (128 KB of K/V in LDS: no room for row-staged
+# Q/O): a2v on 8 register-Q waves (256-query items fill the 256 CUs), audio
+# self-attention on 4.  Gated and ungated.
+RESIDENT_200 = synth.Workload(53, "resident 200 audio keys", 1, 32, 128, 2048, 256, 200)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_resident_keys_unstaged(lt, torch, gated):
+    w = RESIDENT_200
+    inputs = synth.make_block_inputs(w)
+    gates = make_gates(w, 530) if gated else None
+    got = run_block(lt, torch, w, inputs, gates=gates)
+    for k in ("a2v", "audio_self", "v2a"):
+        q, kk, v, L = oracle.pairing(k, inputs, w.audio_kv_len)
+        want = oracle.attention(q, kk, v, kv_len=L, gate=gates[k] if gated else None)
+        compare(got[k], want, f"{w.name}{' gated' if gated else ''} {k}")
+    rng = np.random.default_rng(53)
+    rows = {"video_self": item_rows(rng, 1, w.heads, w.video_len, 256)}
+    want = oracle.block_attention_rows(inputs, w.audio_kv_len, rows,
+                                       gates={"video_self": gates["video_self"]} if gated else None)
+    check_rows(got, want, rows, f"{w.name}{' gated' if gated else ''} every item")
+
+
+# More than 256 valid audio keys: a2v and audio self-attention leave the
+# resident-key kernel for the two-buffer kernel, while video self-attention
+# (288 items of 256 queries) splits its last round -- in the concurrent call
+# the audio side then runs beside that split on the other stream.
+LONG_AUDIO = [synth.Workload(54, "600 audio keys", 1, 8, 128, 9216, 640, 600),
+              synth.Workload(55, "300 audio keys", 1, 8, 128, 9216, 320, 300)]
+
+
+@pytest.mark.parametrize("w", LONG_AUDIO, ids=lambda w: w.name)
+def test_long_audio_sequential_and_overlap(lt, torch, w):
+    inputs = synth.make_block_inputs(w)
+    dev = {n: to_device(a) for n, a in inputs.items()}
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
+    log(f"  GPU block: {w.name}, sequential and overlap")
+    seq = ba(dev, w.audio_kv_len)
+    ovl = ba(dev, w.audio_kv_len, overlap=True)
+    torch.cuda.synchronize()
+    seq = {k: to_numpy(v) for k, v in seq.items()}
+    ovl = {k: to_numpy(v) for k, v in ovl.items()}
+    ba.close()
+    rng = np.random.default_rng(w.cfg)
+    rows = block_item_rows(rng, w)
+    want = oracle.block_attention_rows(inputs, w.audio_kv_len, rows)
+    check_rows(seq, want, rows, f"{w.name} sequential")
+    check_rows(ovl, want, rows, f"{w.name} overlap")
+    for k in KINDS:
+        assert np.array_equal(seq[k], ovl[k]), k
 
 
 TAIL_SPLITS = [
@@ -449,6 +556,20 @@ def test_overlap_matches_sequential(lt, torch, cfg):
     for k in KINDS:
         assert torch.equal(seq[k].view(torch.int16), ovl[k].view(torch.int16)), k
         assert torch.equal(seq_g[k].view(torch.int16), ovl_g[k].view(torch.int16)), k
+    # and the concurrent call's outputs against the oracle itself
+    host_gates = make_gates(w, 200 + cfg)
+    if w.video_len <= 2048:
+        want = oracle.block_attention(inputs, w.audio_kv_len)
+        want_g = oracle.block_attention(inputs, w.audio_kv_len, gates=host_gates)
+        for k in KINDS:
+            compare(to_numpy(ovl[k]), want[k], f"overlap {w.name} {k}")
+            compare(to_numpy(ovl_g[k]), want_g[k], f"overlap gated {w.name} {k}")
+    else:
+        rows = block_item_rows(np.random.default_rng(cfg), w)
+        want = oracle.block_attention_rows(inputs, w.audio_kv_len, rows)
+        want_g = oracle.block_attention_rows(inputs, w.audio_kv_len, rows, gates=host_gates)
+        check_rows({k: to_numpy(v) for k, v in ovl.items()}, want, rows, f"overlap {w.name}")
+        check_rows({k: to_numpy(v) for k, v in ovl_g.items()}, want_g, rows, f"overlap gated {w.name}")
     ba.close()
 
 
@@ -472,6 +593,7 @@ def test_graph_capture_replays(lt, torch, overlap):
     with torch.cuda.graph(g, stream=s):
         ba(dev, w.audio_kv_len, outs=outs, stream=s, overlap=overlap)
     torch.cuda.synchronize()
+    oracle_out = oracle.block_attention(inputs, w.audio_kv_len)
     for rep in range(3):
         for o in outs.values():
             o.zero_()                      # eager work between replays
@@ -480,5 +602,6 @@ def test_graph_capture_replays(lt, torch, overlap):
         torch.cuda.synchronize()
         for k in KINDS:
             assert torch.equal(outs[k].view(torch.int16), want[k].view(torch.int16)), (rep, k)
+            compare(to_numpy(outs[k]), oracle_out[k], f"graph replay {rep} overlap={overlap} {k}")
     del g
     ba.close()

@@ -1151,7 +1151,11 @@ struct Extent {
     uintptr_t lo, hi;
 };
 
-int check_tensor(const ltxattn_tensor &t, int B, int S, int H, int D, Extent *ext) {
+// Layout checks of one [B, S, H, D] tensor; its byte range goes to *ext.
+// An output must also not map two of its (b, s, h) rows onto the same bytes:
+// taking its dimensions of extent > 1 in order of increasing stride, each
+// stride must reach past everything the inner dimensions span.
+int check_tensor(const ltxattn_tensor &t, int B, int S, int H, int D, bool output, Extent *ext) {
     if (!t.data) return LTXATTN_ERR_INVALID_ARG;
     if ((uintptr_t)t.data % 16) return LTXATTN_ERR_INVALID_ARG;
     if (t.stride_b < 0 || t.stride_s < D || t.stride_h < D) return LTXATTN_ERR_INVALID_ARG;
@@ -1161,6 +1165,20 @@ int check_tensor(const ltxattn_tensor &t, int B, int S, int H, int D, Extent *ex
     // byte offsets, so that buffer range checks see every such row.
     const int64_t slice = ((int64_t)(S + BM_MAX + BN) * t.stride_s + D) * 2;
     if (slice >= ((int64_t)1 << 31) - 64) return LTXATTN_ERR_UNSUPPORTED;
+    if (output) {
+        int64_t st[3] = {t.stride_b, t.stride_s, t.stride_h}, ex[3] = {B, S, H};
+        for (int i = 0; i < 3; ++i)   // insertion sort by stride
+            for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
+                std::swap(st[j], st[j - 1]);
+                std::swap(ex[j], ex[j - 1]);
+            }
+        int64_t span = D;   // elements spanned by the dimensions inside the current one
+        for (int i = 0; i < 3; ++i) {
+            if (ex[i] <= 1) continue;
+            if (st[i] < span) return LTXATTN_ERR_INVALID_ARG;
+            span += st[i] * (ex[i] - 1);
+        }
+    }
     const int64_t span = (int64_t)(B - 1) * t.stride_b + (int64_t)(S - 1) * t.stride_s +
                          (int64_t)(H - 1) * t.stride_h + D;
     ext->lo = (uintptr_t)t.data;
@@ -1170,18 +1188,267 @@ int check_tensor(const ltxattn_tensor &t, int B, int S, int H, int D, Extent *ex
 
 bool overlaps(const Extent &x, const Extent &y) { return x.lo < y.hi && y.lo < x.hi; }
 
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+constexpr int LONG_ROWS = 1024;   // query and key rows from which 8-wave workgroups are used
+
+constexpr int RESIDENT_KV_MAX = 4 * BN;   // keys held in LDS by fa_kvres_kernel (128 KB)
+constexpr size_t LDS_BYTES = 160 * 1024;  // LDS per CU on gfx950
+
+// Workspace of split work items, in rows of [D] fp32 partial O plus 2 fp32
+// (m, l).  Region TAIL holds the split last round of video self-attention:
+// its split items fill at most one round of workgroups, num_cus * 256 rows
+// whatever the kernel (8-wave workgroups of 256 queries, or two 4-wave ones of
+// 128 per CU).  Region V2A holds the parts of v2a: items * parts <= num_cus
+// by construction, 128 rows each.
+enum { REGION_NONE = -1, REGION_TAIL = 0, REGION_V2A = 1 };
+// Compute units ltxattn_check_block plans for (no device at hand): MI355X's.
+constexpr int CHECK_CUS = 256;
+int64_t region_rows(int region, int num_cus) {
+    return region == REGION_TAIL ? (int64_t)num_cus * BM_MAX : (int64_t)num_cus * 128;
+}
+
+// The launch of one kind, decided on the host before anything is enqueued.
+struct Plan {
+    const void *kernel = nullptr;   // the attention kernel
+    FaArgs a = {};                  // its arguments (part_o / part_ml set at launch)
+    int threads = 0;
+    size_t lds = 0;                 // dynamic LDS bytes
+    int region = REGION_NONE;       // workspace region of the split parts
+    int64_t ws_rows = 0;            // rows of that region the parts use
+    int bm = 0, n_split_items = 0;  // a combine kernel follows when n_split_items > 0
+};
+
+void fill_args(FaArgs &a, const ltxattn_attn_io &io, int B, int H, int D, int Sq, int kv_len) {
+    a.q = (const __bf16 *)io.q.data;
+    a.k = (const __bf16 *)io.k.data;
+    a.v = (const __bf16 *)io.v.data;
+    a.q_sb = io.q.stride_b; a.q_ss = io.q.stride_s; a.q_sh = io.q.stride_h;
+    a.k_sb = io.k.stride_b; a.k_ss = io.k.stride_s; a.k_sh = io.k.stride_h;
+    a.v_sb = io.v.stride_b; a.v_ss = io.v.stride_s; a.v_sh = io.v.stride_h;
+    a.o = (__bf16 *)io.o.data;
+    a.o_sb = io.o.stride_b; a.o_ss = io.o.stride_s; a.o_sh = io.o.stride_h;
+    a.g = (const __bf16 *)io.gate.data;
+    a.g_sb = io.gate.stride_b; a.g_ss = io.gate.stride_s; a.g_sh = io.gate.stride_h;
+    a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+}
+
+// a2v and audio self-attention: all keys resident in LDS, query tiles streamed.
+Plan plan_resident_kv(int num_cus, int H, int D, const ltxattn_attn_io &io, int B, int Sq, int kv_len) {
+    Plan p;
+    FaArgs &a = p.a;
+    fill_args(a, io, B, H, D, Sq, kv_len);
+    const int nkt = ceil_div(kv_len, BN);
+    const size_t kv_lds = (size_t)nkt * 2 * BN * D * 2;
+    // D = 128: 8 waves, two per SIMD, with Q and O rows staged through one
+    // 8 KB slot per wave when the keys leave room for the slots, else with
+    // Q straight from HBM into registers (up to 256 keys: 128 KB of K/V) --
+    // or 4 such waves when 256-query items would leave most CUs idle (a
+    // short query stream such as audio self-attention).  D = 64: 4 unstaged
+    // waves.
+    const bool staged = D == 128 && kv_lds + 8 * KVRES_SLOT <= LDS_BYTES;
+    const int nw = staged || (D == 128 && (int64_t)B * H * ceil_div(Sq, 256) >= num_cus) ? 8 : 4;
+    p.lds = kv_lds + (staged ? (size_t)8 * KVRES_SLOT : 0);
+    a.n_qtiles = ceil_div(Sq, 32 * nw);
+    const int items = B * H * a.n_qtiles;
+    const int per_cu = (int)std::min<size_t>(2, LDS_BYTES / p.lds);   // LDS-resident workgroups per CU
+    a.groups = (items % 8 == 0 && num_cus % 8 == 0) ? 8 : 1;
+    a.ipg = items / a.groups;
+    const int per_group = std::min(a.ipg, (nw == 8 ? 1 : per_cu) * num_cus / a.groups);
+    a.total = a.groups * per_group;
+    p.threads = 64 * nw;
+    // Gated outputs take instantiations of their own, so that the ungated
+    // ones are compiled without any gate code.
+    const bool g = a.g != nullptr;
+    if (D == 128 && staged)
+        p.kernel = g ? (const void *)&fa_kvres_kernel<128, 8, true, true> : (const void *)&fa_kvres_kernel<128, 8, true, false>;
+    else if (D == 128 && nw == 8)
+        p.kernel = g ? (const void *)&fa_kvres_kernel<128, 8, false, true> : (const void *)&fa_kvres_kernel<128, 8, false, false>;
+    else if (D == 128)
+        p.kernel = g ? (const void *)&fa_kvres_kernel<128, 4, false, true> : (const void *)&fa_kvres_kernel<128, 4, false, false>;
+    else
+        p.kernel = g ? (const void *)&fa_kvres_kernel<64, 4, false, true> : (const void *)&fa_kvres_kernel<64, 4, false, false>;
+    return p;
+}
+
+// v2a: one workgroup per CU streams one key range of one 128-query item
+// (fa_ring_kernel with two key groups); as many ranges per item as fill the CUs.
+Plan plan_stream(int num_cus, int H, int D, const ltxattn_attn_io &io, int B, int Sq, int kv_len) {
+    Plan p;
+    FaArgs &a = p.a;
+    fill_args(a, io, B, H, D, Sq, kv_len);
+    const int BM = 128;
+    a.n_qtiles = ceil_div(Sq, BM);
+    const int items = B * H * a.n_qtiles;
+    a.groups = (items % 8 == 0 && num_cus % 8 == 0) ? 8 : 1;
+    a.ipg = items / a.groups;
+    // Parts per item: one workgroup per CU, at most NSPLIT_MAX, at least
+    // four key tiles per part.
+    int ns = num_cus / items;
+    ns = ns < NSPLIT_MAX ? ns : NSPLIT_MAX;
+    const int by_len = kv_len / (4 * BN);
+    ns = ns < by_len ? ns : by_len;
+    ns = ns < 1 ? 1 : ns;
+    a.split_len = ceil_div(ceil_div(kv_len, ns), BN) * BN;
+    ns = ceil_div(kv_len, a.split_len);    // every part holds at least one key
+    a.nsplit = ns;
+    a.wpg = ns == 1 ? a.ipg : 0;           // one part: every item is whole
+    a.total = items * ns;
+    p.threads = 64 * RING_NW;
+    p.lds = (size_t)RING_STAGES * 2 * BN * D * 2;
+    p.kernel = D == 128 ? (const void *)&fa_ring_kernel<128, RING_NW, 2> : (const void *)&fa_ring_kernel<64, RING_NW, 2>;
+    if (ns > 1) {
+        p.region = REGION_V2A;
+        p.ws_rows = (int64_t)items * ns * BM;
+        p.bm = BM;
+        p.n_split_items = items;
+    }
+    return p;
+}
+
+// One kind's launch.  v2a takes the split-KV stream; a short key stream the
+// resident-key kernel; otherwise the ring kernel (long query and key
+// streams at D = 128: 256-query workgroups, so each K/V tile is fetched
+// once per 256 queries) or fa_fwd_kernel (128 queries).  With tail_split,
+// the items of an incomplete last round may run as key-range parts in the
+// TAIL region; only video self-attention does this, so that no other kind
+// shares that region with it when the audio side runs on its own stream.
+Plan plan_kind(int num_cus, int H, int D, const ltxattn_attn_io &io, int B, int Sq, int kv_len,
+               bool split_all, bool tail_split) {
+    if (split_all) return plan_stream(num_cus, H, D, io, B, Sq, kv_len);
+    if (kv_len <= RESIDENT_KV_MAX) return plan_resident_kv(num_cus, H, D, io, B, Sq, kv_len);
+    Plan p;
+    FaArgs &a = p.a;
+    fill_args(a, io, B, H, D, Sq, kv_len);
+    const int NW = (Sq >= LONG_ROWS && kv_len >= LONG_ROWS && D == 128) ? 8 : 4;
+    const int BM = 32 * NW;
+    a.n_qtiles = ceil_div(Sq, BM);
+    const int items = B * H * a.n_qtiles;
+    // One group per XCD when the items divide evenly, else a single group.
+    const int groups = (items % 8 == 0 && num_cus % 8 == 0) ? 8 : 1;
+    const int ipg = items / groups;
+    const int slots = WAVES_PER_CU / NW * num_cus / groups;   // workgroups resident per group
+    int spg = 0, ns = 1;                                 // split items per group, parts each
+    if (tail_split && ipg > slots) {
+        // Split the items of an incomplete last round so that it fills its XCD.
+        const int rem = ipg % slots;
+        if (rem > 0 && 2 * rem <= slots) {
+            ns = slots / rem;
+            ns = ns < NSPLIT_MAX ? ns : NSPLIT_MAX;
+            const int by_len = kv_len / (4 * BN);
+            ns = ns < by_len ? ns : by_len;
+            if (ns > 1) spg = rem;
+        }
+    }
+    if (spg == 0) ns = 1;
+    a.split_len = ceil_div(ceil_div(kv_len, ns), BN) * BN;
+    ns = ceil_div(kv_len, a.split_len);   // every part holds at least one key
+    if (ns == 1) spg = 0;
+    a.nsplit = ns;
+    a.groups = groups;
+    a.ipg = ipg;
+    a.wpg = ipg - spg;
+    // Two parts per split item on exactly half of each group's CUs: deal
+    // them first and last (measured: 0.4-1% off the video kernel).
+    a.stagger = D == 128 && NW == 8 && ns == 2 && 2 * spg == slots;
+    a.total = groups * (a.wpg + spg * ns);
+    const int n_split_items = groups * spg;
+    if (n_split_items > 0) {
+        p.region = REGION_TAIL;
+        p.ws_rows = (int64_t)n_split_items * ns * BM;
+        p.bm = BM;
+        p.n_split_items = n_split_items;
+    }
+    if (D == 128 && NW == 8) {
+        p.kernel = (const void *)&fa_ring_kernel<128, RING_NW, 1>;
+        p.threads = 64 * RING_NW;
+        p.lds = (size_t)RING_STAGES * 2 * BN * 128 * 2;
+    } else {
+        p.kernel = D == 128 ? (const void *)&fa_fwd_kernel<128, 4> : (const void *)&fa_fwd_kernel<64, 4>;
+        p.threads = 256;
+    }
+    return p;
+}
+
+// Launch order of the kinds.  v2a runs straight after video self-attention:
+// it streams the same video K and V, part of which the last-level cache
+// still holds; a2v, which writes a video-sized output, comes after it.
+constexpr int KIND_ORDER[4] = {LTXATTN_VIDEO_SELF, LTXATTN_V2A, LTXATTN_A2V, LTXATTN_AUDIO_SELF};
+
+// The plan of every kind whose output is given (on[k]) for a device with
+// num_cus compute units.
+void plan_block(const ltxattn_config &caps, const ltxattn_block_io *io, const bool on[4], int num_cus,
+                Plan plans[4]) {
+    const int B = io->batch, Sv = io->video_len, La = io->audio_len, Lk = io->audio_kv_len;
+    const int q_rows[4] = {Sv, La, Sv, La};
+    for (int k = 0; k < 4; ++k) {
+        if (!on[k]) continue;
+        const int kv_len = (k == LTXATTN_AUDIO_SELF || k == LTXATTN_A2V) ? Lk : Sv;
+        plans[k] = plan_kind(num_cus, caps.heads, caps.head_dim, io->attn[k], B, q_rows[k], kv_len,
+                             k == LTXATTN_V2A, k == LTXATTN_VIDEO_SELF);
+    }
+}
+
+// Argument checks shared by ltxattn_check_block and the block calls, then
+// the workspace each kind's split parts need against the rows a workspace
+// for num_cus compute units has per region.  on[k] is set for the kinds
+// whose output pointer is non-null.
+int validate_block(const ltxattn_config &caps, const ltxattn_block_io *io, int num_cus, bool on[4]) {
+    const int B = io->batch, Sv = io->video_len, La = io->audio_len, Lk = io->audio_kv_len;
+    if (B < 1 || B > caps.max_batch) return LTXATTN_ERR_INVALID_ARG;
+    if (Sv < 1 || Sv > caps.max_video_len) return LTXATTN_ERR_INVALID_ARG;
+    if (La < 1 || La > caps.max_audio_len) return LTXATTN_ERR_INVALID_ARG;
+    if (Lk < 1 || Lk > La) return LTXATTN_ERR_INVALID_ARG;
+    const int H = caps.heads, D = caps.head_dim;
+    // Rows of q/o and of k/v per kind.
+    const int q_rows[4] = {Sv, La, Sv, La};
+    const int kv_rows[4] = {Sv, La, La, Sv};
+    Extent in_ext[4][4] = {}, out_ext[4];
+    for (int k = 0; k < 4; ++k) {
+        const ltxattn_attn_io &x = io->attn[k];
+        on[k] = x.o.data != nullptr;
+        if (!on[k]) continue;
+        int rc;
+        if ((rc = check_tensor(x.q, B, q_rows[k], H, D, false, &in_ext[k][0]))) return rc;
+        if ((rc = check_tensor(x.k, B, kv_rows[k], H, D, false, &in_ext[k][1]))) return rc;
+        if ((rc = check_tensor(x.v, B, kv_rows[k], H, D, false, &in_ext[k][2]))) return rc;
+        if ((rc = check_tensor(x.o, B, q_rows[k], H, D, true, &out_ext[k]))) return rc;
+        if (x.gate.data && (rc = check_tensor(x.gate, B, q_rows[k], H, D, false, &in_ext[k][3]))) return rc;
+    }
+    for (int k = 0; k < 4; ++k) {
+        if (!on[k]) continue;
+        for (int j = 0; j < 4; ++j) {
+            if (!on[j]) continue;
+            for (int t = 0; t < 4; ++t)   // q, k, v, gate (an absent gate spans nothing)
+                if (overlaps(out_ext[k], in_ext[j][t])) return LTXATTN_ERR_INVALID_ARG;
+            if (j != k && overlaps(out_ext[k], out_ext[j])) return LTXATTN_ERR_INVALID_ARG;
+        }
+    }
+    Plan plans[4];
+    plan_block(caps, io, on, num_cus, plans);
+    for (int k = 0; k < 4; ++k)
+        if (on[k] && plans[k].region != REGION_NONE && plans[k].ws_rows > region_rows(plans[k].region, num_cus))
+            return LTXATTN_ERR_UNSUPPORTED;
+    return LTXATTN_OK;
+}
+
+// The workspace of split parts: two regions, TAIL then V2A, of rows[r] rows
+// each, as [rows][D] fp32 partial outputs in o and [rows][2] fp32 (m, l) in ml.
+struct Workspace {
+    float *o, *ml;
+    int64_t rows[2];
+};
+
 }  // namespace
 
 struct ltxattn_handle {
     int device;
     int heads, head_dim, max_batch, max_video_len, max_audio_len;
     int num_cus;
-    // Workspace of split items, two regions so that v2a can run beside the
-    // other kinds: rows [0, tail_rows) for the split last round of a
-    // self-attention, rows [tail_rows, tail_rows + v2a_rows) for v2a.
-    float *ws_o;      // [rows][head_dim]
-    float *ws_ml;     // [rows][2]
-    int64_t tail_rows, v2a_rows;
+    // Workspace of split items (hipMalloc at create), in two regions so that
+    // v2a can run beside video self-attention.
+    Workspace ws;
     // ltxattn_block_attention_overlap: the stream the audio-side kinds run
     // on, and the events that fork it from and join it to the caller's.
     hipStream_t side;
@@ -1225,270 +1492,61 @@ int hip_fail(ltxattn_handle *h, hipError_t e) {
     return LTXATTN_ERR_HIP;
 }
 
-int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
-
-constexpr int LONG_ROWS = 1024;   // query and key rows from which 8-wave workgroups are used
-
-constexpr int RESIDENT_KV_MAX = 4 * BN;   // keys held in LDS by fa_kvres_kernel (128 KB)
-constexpr size_t LDS_BYTES = 160 * 1024;  // LDS per CU on gfx950
-
-// a2v and audio self-attention: all keys resident in LDS, query tiles streamed.
-int run_resident_kv(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len, hipStream_t st) {
-    const int D = h->head_dim, H = h->heads;
-    FaArgs a = {};
-    a.q = (const __bf16 *)io.q.data;
-    a.k = (const __bf16 *)io.k.data;
-    a.v = (const __bf16 *)io.v.data;
-    a.q_sb = io.q.stride_b; a.q_ss = io.q.stride_s; a.q_sh = io.q.stride_h;
-    a.k_sb = io.k.stride_b; a.k_ss = io.k.stride_s; a.k_sh = io.k.stride_h;
-    a.v_sb = io.v.stride_b; a.v_ss = io.v.stride_s; a.v_sh = io.v.stride_h;
-    a.o = (__bf16 *)io.o.data;
-    a.o_sb = io.o.stride_b; a.o_ss = io.o.stride_s; a.o_sh = io.o.stride_h;
-    a.g = (const __bf16 *)io.gate.data;
-    a.g_sb = io.gate.stride_b; a.g_ss = io.gate.stride_s; a.g_sh = io.gate.stride_h;
-    a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
-    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    const int nkt = ceil_div(kv_len, BN);
-    const size_t kv_lds = (size_t)nkt * 2 * BN * D * 2;
-    // D = 128: 8 waves, two per SIMD, with Q and O rows staged through one
-    // 8 KB slot per wave when the keys leave room for the slots, else with
-    // Q straight from HBM into registers (up to 256 keys: 128 KB of K/V) --
-    // or 4 such waves when 256-query items would leave most CUs idle (a
-    // short query stream such as audio self-attention).  D = 64: 4 unstaged
-    // waves.
-    const bool staged = D == 128 && kv_lds + 8 * KVRES_SLOT <= LDS_BYTES;
-    const int nw = staged || (D == 128 && (int64_t)B * H * ceil_div(Sq, 256) >= h->num_cus) ? 8 : 4;
-    const size_t lds = kv_lds + (staged ? (size_t)8 * KVRES_SLOT : 0);
-    a.n_qtiles = ceil_div(Sq, 32 * nw);
-    const int items = B * H * a.n_qtiles;
-    const int per_cu = (int)std::min<size_t>(2, LDS_BYTES / lds);   // LDS-resident workgroups per CU
-    a.groups = (items % 8 == 0 && h->num_cus % 8 == 0) ? 8 : 1;
-    a.ipg = items / a.groups;
-    const int per_group = std::min(a.ipg, (nw == 8 ? 1 : per_cu) * h->num_cus / a.groups);
-    a.total = a.groups * per_group;
-    // Gated outputs take instantiations of their own, so that the ungated
-    // ones are compiled without any gate code.
-    if (a.g) {
-        if (D == 128 && staged)
-            hipLaunchKernelGGL((fa_kvres_kernel<128, 8, true, true>), dim3(a.total), dim3(512), lds, st, a);
-        else if (D == 128 && nw == 8)
-            hipLaunchKernelGGL((fa_kvres_kernel<128, 8, false, true>), dim3(a.total), dim3(512), lds, st, a);
-        else if (D == 128) hipLaunchKernelGGL((fa_kvres_kernel<128, 4, false, true>), dim3(a.total), dim3(256), lds, st, a);
-        else hipLaunchKernelGGL((fa_kvres_kernel<64, 4, false, true>), dim3(a.total), dim3(256), lds, st, a);
-    } else if (D == 128 && staged)
-        hipLaunchKernelGGL((fa_kvres_kernel<128, 8, true, false>), dim3(a.total), dim3(512), lds, st, a);
-    else if (D == 128 && nw == 8)
-        hipLaunchKernelGGL((fa_kvres_kernel<128, 8, false, false>), dim3(a.total), dim3(512), lds, st, a);
-    else if (D == 128) hipLaunchKernelGGL((fa_kvres_kernel<128, 4, false, false>), dim3(a.total), dim3(256), lds, st, a);
-    else hipLaunchKernelGGL((fa_kvres_kernel<64, 4, false, false>), dim3(a.total), dim3(256), lds, st, a);
-    const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? LTXATTN_OK : hip_fail(h, e);
-}
-
-// Merge the key-range parts of n_split_items items (fa_combine_kernel).
-int run_combine(ltxattn_handle *h, const FaArgs &a, int bm, int n_split_items, hipStream_t st) {
-    CombineArgs c;
-    c.part_o = a.part_o; c.part_ml = a.part_ml;
-    c.o = a.o; c.o_sb = a.o_sb; c.o_ss = a.o_ss; c.o_sh = a.o_sh;
-    c.g = a.g; c.g_sb = a.g_sb; c.g_ss = a.g_ss; c.g_sh = a.g_sh;
-    c.H = a.H; c.Sq = a.Sq; c.bm = bm; c.n_qtiles = a.n_qtiles; c.ipg = a.ipg; c.wpg = a.wpg;
-    c.n_split_items = n_split_items; c.nsplit = a.nsplit;
-    const int64_t threads = (int64_t)n_split_items * bm * (h->head_dim / 4);
-    const int grid = ceil_div(threads, 256);
-    if (h->head_dim == 128) hipLaunchKernelGGL((fa_combine_kernel<128>), dim3(grid), dim3(256), 0, st, c);
-    else hipLaunchKernelGGL((fa_combine_kernel<64>), dim3(grid), dim3(256), 0, st, c);
-    const hipError_t e = hipGetLastError();
-    return e == hipSuccess ? LTXATTN_OK : hip_fail(h, e);
-}
-
-// v2a: one workgroup per CU streams one key range of one 128-query item
-// (fa_ring_kernel with two key groups); as many ranges per item as fill the CUs.
-int run_stream(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len, hipStream_t st,
-               hipEvent_t after_main, bool *mid_recorded) {
-    const int D = h->head_dim, H = h->heads, BM = 128;
-    FaArgs a = {};
-    a.q = (const __bf16 *)io.q.data;
-    a.k = (const __bf16 *)io.k.data;
-    a.v = (const __bf16 *)io.v.data;
-    a.q_sb = io.q.stride_b; a.q_ss = io.q.stride_s; a.q_sh = io.q.stride_h;
-    a.k_sb = io.k.stride_b; a.k_ss = io.k.stride_s; a.k_sh = io.k.stride_h;
-    a.v_sb = io.v.stride_b; a.v_ss = io.v.stride_s; a.v_sh = io.v.stride_h;
-    a.o = (__bf16 *)io.o.data;
-    a.o_sb = io.o.stride_b; a.o_ss = io.o.stride_s; a.o_sh = io.o.stride_h;
-    a.g = (const __bf16 *)io.gate.data;
-    a.g_sb = io.gate.stride_b; a.g_ss = io.gate.stride_s; a.g_sh = io.gate.stride_h;
-    a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
-    a.n_qtiles = ceil_div(Sq, BM);
-    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    const int items = B * H * a.n_qtiles;
-    a.groups = (items % 8 == 0 && h->num_cus % 8 == 0) ? 8 : 1;
-    a.ipg = items / a.groups;
-    // Parts per item: one workgroup per CU, at most NSPLIT_MAX, at least
-    // four key tiles per part.
-    int ns = h->num_cus / items;
-    ns = ns < NSPLIT_MAX ? ns : NSPLIT_MAX;
-    const int by_len = kv_len / (4 * BN);
-    ns = ns < by_len ? ns : by_len;
-    ns = ns < 1 ? 1 : ns;
-    a.split_len = ceil_div(ceil_div(kv_len, ns), BN) * BN;
-    ns = ceil_div(kv_len, a.split_len);    // every part holds at least one key
-    a.nsplit = ns;
-    a.wpg = ns == 1 ? a.ipg : 0;           // one part: every item is whole
-    a.part_o = h->ws_o + h->tail_rows * D;  // the v2a region of the workspace
-    a.part_ml = h->ws_ml + h->tail_rows * 2;
-    a.total = items * ns;
-    if (ns > 1 && (int64_t)items * ns * BM > h->v2a_rows) return LTXATTN_ERR_INVALID_ARG;  // cannot happen
-    const size_t lds = (size_t)RING_STAGES * 2 * BN * D * 2;
-    if (D == 128) hipLaunchKernelGGL((fa_ring_kernel<128, RING_NW, 2>), dim3(a.total), dim3(64 * RING_NW), lds, st, a);
-    else hipLaunchKernelGGL((fa_ring_kernel<64, RING_NW, 2>), dim3(a.total), dim3(64 * RING_NW), lds, st, a);
-    hipError_t e = hipGetLastError();
+// Launch one planned kind on stream st, with its split parts (if any) in
+// its region of ws, then the combine kernel that merges them.  When
+// `after_main` is given and a combine kernel follows, the event is recorded
+// between the two and *mid_recorded is set.
+int launch_plan(ltxattn_handle *h, const Plan &p, const Workspace &ws, hipStream_t st, hipEvent_t after_main,
+                bool *mid_recorded) {
+    const int D = h->head_dim;
+    FaArgs a = p.a;
+    if (p.region != REGION_NONE) {
+        const int64_t r0 = p.region == REGION_V2A ? ws.rows[REGION_TAIL] : 0;
+        a.part_o = ws.o + r0 * D;
+        a.part_ml = ws.ml + r0 * 2;
+    }
+    void *args[] = {&a};
+    hipError_t e = hipLaunchKernel(p.kernel, dim3(a.total), dim3(p.threads), args, p.lds, st);
     if (e != hipSuccess) return hip_fail(h, e);
-    if (ns == 1) return LTXATTN_OK;
+    if (p.n_split_items == 0) return LTXATTN_OK;
     if (after_main) {
         if ((e = hipEventRecord(after_main, st)) != hipSuccess) return hip_fail(h, e);
         *mid_recorded = true;
     }
-    return run_combine(h, a, BM, items, st);
+    // Merge the key-range parts of the split items (fa_combine_kernel).
+    CombineArgs c;
+    c.part_o = a.part_o; c.part_ml = a.part_ml;
+    c.o = a.o; c.o_sb = a.o_sb; c.o_ss = a.o_ss; c.o_sh = a.o_sh;
+    c.g = a.g; c.g_sb = a.g_sb; c.g_ss = a.g_ss; c.g_sh = a.g_sh;
+    c.H = a.H; c.Sq = a.Sq; c.bm = p.bm; c.n_qtiles = a.n_qtiles; c.ipg = a.ipg; c.wpg = a.wpg;
+    c.n_split_items = p.n_split_items; c.nsplit = a.nsplit;
+    const int64_t threads = (int64_t)p.n_split_items * p.bm * (D / 4);
+    void *cargs[] = {&c};
+    e = hipLaunchKernel(D == 128 ? (const void *)&fa_combine_kernel<128> : (const void *)&fa_combine_kernel<64>,
+                        dim3(ceil_div(threads, 256)), dim3(256), cargs, 0, st);
+    return e == hipSuccess ? LTXATTN_OK : hip_fail(h, e);
 }
 
-// Launches the attention kernel for one kind and, if some items were split,
-// the combine kernel.  When `after_main` is given and a combine kernel
-// follows, the event is recorded between the two and *mid_recorded is set.
-int run_attention(ltxattn_handle *h, const ltxattn_attn_io &io, int B, int Sq, int kv_len,
-                  bool split_all, hipStream_t st, hipEvent_t after_main, bool *mid_recorded) {
-    const int D = h->head_dim, H = h->heads;
-    if (split_all) return run_stream(h, io, B, Sq, kv_len, st, after_main, mid_recorded);
-    if (kv_len <= RESIDENT_KV_MAX) return run_resident_kv(h, io, B, Sq, kv_len, st);
-    // Long query and key streams (video self-attention) take the ring kernel
-    // with 256-query workgroups: each K/V tile is then fetched once per 256
-    // queries.  Other shapes take fa_fwd_kernel with 128.
-    const int NW = (Sq >= LONG_ROWS && kv_len >= LONG_ROWS && D == 128) ? 8 : 4;
-    const int BM = 32 * NW;
-    FaArgs a = {};
-    a.q = (const __bf16 *)io.q.data;
-    a.k = (const __bf16 *)io.k.data;
-    a.v = (const __bf16 *)io.v.data;
-    a.q_sb = io.q.stride_b; a.q_ss = io.q.stride_s; a.q_sh = io.q.stride_h;
-    a.k_sb = io.k.stride_b; a.k_ss = io.k.stride_s; a.k_sh = io.k.stride_h;
-    a.v_sb = io.v.stride_b; a.v_ss = io.v.stride_s; a.v_sh = io.v.stride_h;
-    a.o = (__bf16 *)io.o.data;
-    a.o_sb = io.o.stride_b; a.o_ss = io.o.stride_s; a.o_sh = io.o.stride_h;
-    a.g = (const __bf16 *)io.gate.data;
-    a.g_sb = io.gate.stride_b; a.g_ss = io.gate.stride_s; a.g_sh = io.gate.stride_h;
-    a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
-    a.n_qtiles = ceil_div(Sq, BM);
-    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    const int items = B * H * a.n_qtiles;
-    // One group per XCD when the items divide evenly, else a single group.
-    const int groups = (items % 8 == 0 && h->num_cus % 8 == 0) ? 8 : 1;
-    const int ipg = items / groups;
-    const int slots = WAVES_PER_CU / NW * h->num_cus / groups;   // workgroups resident per group
-    int spg = 0, ns = 1;                                 // split items per group, parts each
-    if (ipg > slots) {
-        // Split the items of an incomplete last round so that it fills its XCD.
-        const int rem = ipg % slots;
-        if (rem > 0 && 2 * rem <= slots) {
-            ns = slots / rem;
-            ns = ns < NSPLIT_MAX ? ns : NSPLIT_MAX;
-            const int by_len = kv_len / (4 * BN);
-            ns = ns < by_len ? ns : by_len;
-            if (ns > 1) spg = rem;
-        }
-    }
-    if (spg == 0) ns = 1;
-    a.split_len = ceil_div(ceil_div(kv_len, ns), BN) * BN;
-    ns = ceil_div(kv_len, a.split_len);   // every part holds at least one key
-    if (ns == 1) spg = 0;
-    a.nsplit = ns;
-    a.groups = groups;
-    a.ipg = ipg;
-    a.wpg = ipg - spg;
-    // Two parts per split item on exactly half of each group's CUs: deal
-    // them first and last (measured: 0.4-1% off the video kernel).
-    a.stagger = D == 128 && NW == 8 && ns == 2 && 2 * spg == slots;
-    a.part_o = h->ws_o;                    // the tail region of the workspace
-    a.part_ml = h->ws_ml;
-    a.total = groups * (a.wpg + spg * ns);
-    const int n_split_items = groups * spg;
-    if ((int64_t)n_split_items * ns * BM > h->tail_rows) return LTXATTN_ERR_INVALID_ARG;  // cannot happen
-
-    if (D == 128 && NW == 8)
-        hipLaunchKernelGGL((fa_ring_kernel<128, RING_NW, 1>), dim3(a.total), dim3(64 * RING_NW),
-                           (size_t)RING_STAGES * 2 * BN * 128 * 2, st, a);
-    else if (D == 128) hipLaunchKernelGGL((fa_fwd_kernel<128, 4>), dim3(a.total), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((fa_fwd_kernel<64, 4>), dim3(a.total), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(h, e);
-    if (n_split_items > 0) {
-        if (after_main) {
-            if ((e = hipEventRecord(after_main, st)) != hipSuccess) return hip_fail(h, e);
-            *mid_recorded = true;
-        }
-        return run_combine(h, a, BM, n_split_items, st);
-    }
-    return LTXATTN_OK;
-}
-
-// Launch order of the kinds.  v2a runs straight after video self-attention:
-// it streams the same video K and V, part of which the last-level cache
-// still holds; a2v, which writes a video-sized output, comes after it.
-constexpr int KIND_ORDER[4] = {LTXATTN_VIDEO_SELF, LTXATTN_V2A, LTXATTN_A2V, LTXATTN_AUDIO_SELF};
-
-// Argument checks shared by ltxattn_check_block and ltxattn_block_attention.
-// on[k] is set for the kinds whose output pointer is non-null.
-int validate_block(const ltxattn_config &caps, const ltxattn_block_io *io, bool on[4]) {
-    const int B = io->batch, Sv = io->video_len, La = io->audio_len, Lk = io->audio_kv_len;
-    if (B < 1 || B > caps.max_batch) return LTXATTN_ERR_INVALID_ARG;
-    if (Sv < 1 || Sv > caps.max_video_len) return LTXATTN_ERR_INVALID_ARG;
-    if (La < 1 || La > caps.max_audio_len) return LTXATTN_ERR_INVALID_ARG;
-    if (Lk < 1 || Lk > La) return LTXATTN_ERR_INVALID_ARG;
-    const int H = caps.heads, D = caps.head_dim;
-    // Rows of q/o and of k/v per kind.
-    const int q_rows[4] = {Sv, La, Sv, La};
-    const int kv_rows[4] = {Sv, La, La, Sv};
-    Extent in_ext[4][4] = {}, out_ext[4];
-    for (int k = 0; k < 4; ++k) {
-        const ltxattn_attn_io &x = io->attn[k];
-        on[k] = x.o.data != nullptr;
-        if (!on[k]) continue;
-        int rc;
-        if ((rc = check_tensor(x.q, B, q_rows[k], H, D, &in_ext[k][0]))) return rc;
-        if ((rc = check_tensor(x.k, B, kv_rows[k], H, D, &in_ext[k][1]))) return rc;
-        if ((rc = check_tensor(x.v, B, kv_rows[k], H, D, &in_ext[k][2]))) return rc;
-        if ((rc = check_tensor(x.o, B, q_rows[k], H, D, &out_ext[k]))) return rc;
-        if (x.gate.data && (rc = check_tensor(x.gate, B, q_rows[k], H, D, &in_ext[k][3]))) return rc;
-    }
-    for (int k = 0; k < 4; ++k) {
-        if (!on[k]) continue;
-        for (int j = 0; j < 4; ++j) {
-            if (!on[j]) continue;
-            for (int t = 0; t < 4; ++t)   // q, k, v, gate (an absent gate spans nothing)
-                if (overlaps(out_ext[k], in_ext[j][t])) return LTXATTN_ERR_INVALID_ARG;
-            if (j != k && overlaps(out_ext[k], out_ext[j])) return LTXATTN_ERR_INVALID_ARG;
-        }
-    }
-    return LTXATTN_OK;
-}
-
-// The block call.  Kinds run in KIND_ORDER on the caller's stream; with
-// `overlap`, the audio-side kinds (v2a, a2v, audio self) run on the
-// handle's side stream instead, forked from the caller's stream at the
-// start of the call and joined back into it at the end, so the call stays
-// one ordered unit on the caller's stream (and can be captured into a HIP
-// graph from it).  Profiling events, if on, are recorded in enqueue order
-// and indexed per call by ProfCall: the call's start and end (when every
-// kind is recorded), and for each recorded kind its start, the end of its
-// attention kernel when a combine kernel follows, and its end, on the
-// stream that runs it.
+// The block call.  Every argument and the workspace of every kind are
+// checked, and every kind planned, before anything is enqueued.  Kinds run
+// in KIND_ORDER on the caller's stream; with `overlap`, the audio-side kinds
+// (v2a, a2v, audio self) run on the handle's side stream instead, forked
+// from the caller's stream at the start of the call and joined back into it
+// at the end, so the call stays one ordered unit on the caller's stream (and
+// can be captured into a HIP graph from it).  Profiling events, if on, are
+// recorded in enqueue order and indexed per call by ProfCall: the call's
+// start and end (when every kind is recorded), and for each recorded kind
+// its start, the end of its attention kernel when a combine kernel follows,
+// and its end, on the stream that runs it.
 int enqueue_block(ltxattn_handle *h, const ltxattn_block_io *io, hipStream_t st, bool overlap) {
     if (!h || !io) return LTXATTN_ERR_INVALID_ARG;
     const ltxattn_config caps = {h->device, h->heads, h->head_dim, h->max_batch, h->max_video_len,
                                  h->max_audio_len};
     bool on[4];
-    const int vrc = validate_block(caps, io, on);
+    const int vrc = validate_block(caps, io, h->num_cus, on);
     if (vrc) return vrc;
-    const int B = io->batch, Sv = io->video_len, La = io->audio_len, Lk = io->audio_kv_len;
-    const int q_rows[4] = {Sv, La, Sv, La};
+    Plan plans[4];
+    plan_block(caps, io, on, h->num_cus, plans);
 
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return hip_fail(h, g.err);
@@ -1532,10 +1590,8 @@ int enqueue_block(ltxattn_handle *h, const ltxattn_block_io *io, hipStream_t st,
         }
         if (e != hipSuccess) return hip_fail(h, e);
         if (!on[k]) continue;
-        const int kv_len = (k == LTXATTN_AUDIO_SELF || k == LTXATTN_A2V) ? Lk : Sv;
         bool mid_rec = false;
-        const int rc = run_attention(h, io->attn[k], B, q_rows[k], kv_len, k == LTXATTN_V2A, ks,
-                                     rec_k ? ev[n_ev] : nullptr, rec_k ? &mid_rec : nullptr);
+        const int rc = launch_plan(h, plans[k], h->ws, ks, rec_k ? ev[n_ev] : nullptr, rec_k ? &mid_rec : nullptr);
         if (rc) return rc;
         if (rec_k) {
             if (mid_rec) pc->mid[k] = (int8_t)n_ev++;
@@ -1565,8 +1621,8 @@ hipError_t release(ltxattn_handle *h) {
     if (h->join) keep(hipEventDestroy(h->join));
     if (h->fork) keep(hipEventDestroy(h->fork));
     if (h->side) keep(hipStreamDestroy(h->side));
-    if (h->ws_ml) keep(hipFree(h->ws_ml));
-    if (h->ws_o) keep(hipFree(h->ws_o));
+    if (h->ws.ml) keep(hipFree(h->ws.ml));
+    if (h->ws.o) keep(hipFree(h->ws.o));
     free(h);
     return first;
 }
@@ -1633,15 +1689,14 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
         e = hipFuncSetAttribute((const void *)&fa_ring_kernel<128, RING_NW, 1>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 128 * 2);
     if (e != hipSuccess) { g_create_hip_error = (int)e; free(h); return LTXATTN_ERR_HIP; }
-    // Workspace of the split items, BM rows per part: the tail split of a
-    // self-attention uses at most one round of workgroups; v2a splits every
-    // audio query tile of every (batch, head) into at most NSPLIT_MAX parts.
-    h->tail_rows = (int64_t)WAVES_PER_CU / 4 * h->num_cus * BM_MAX;
-    h->v2a_rows = (int64_t)h->max_batch * h->heads * ceil_div(h->max_audio_len, 128) * NSPLIT_MAX * 128;
-    const int64_t rows = h->tail_rows + h->v2a_rows;
+    // Workspace of the split items: both regions at their bounds for this
+    // device's compute units.
+    h->ws.rows[REGION_TAIL] = region_rows(REGION_TAIL, h->num_cus);
+    h->ws.rows[REGION_V2A] = region_rows(REGION_V2A, h->num_cus);
+    const int64_t rows = h->ws.rows[REGION_TAIL] + h->ws.rows[REGION_V2A];
     int status = LTXATTN_OK;
-    e = hipMalloc((void **)&h->ws_o, (size_t)rows * h->head_dim * sizeof(float));
-    if (e == hipSuccess) e = hipMalloc((void **)&h->ws_ml, (size_t)rows * 2 * sizeof(float));
+    e = hipMalloc((void **)&h->ws.o, (size_t)rows * h->head_dim * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void **)&h->ws.ml, (size_t)rows * 2 * sizeof(float));
     if (e != hipSuccess) status = LTXATTN_ERR_OOM;
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
@@ -1670,7 +1725,7 @@ int ltxattn_check_block(const ltxattn_config *cfg, const ltxattn_block_io *io) {
     if (cfg->head_dim != 64 && cfg->head_dim != 128) return LTXATTN_ERR_UNSUPPORTED;
     if (cfg->heads < 1) return LTXATTN_ERR_UNSUPPORTED;
     bool on[4];
-    return validate_block(*cfg, io, on);
+    return validate_block(*cfg, io, CHECK_CUS, on);
 }
 
 int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void *hip_stream) {
