@@ -60,6 +60,8 @@ extern "C" {
 #define LTXATTN_ERR_HIP         (-3) /* a HIP call or kernel launch failed; see
                                         ltxattn_last_hip_error */
 #define LTXATTN_ERR_OOM         (-4) /* device workspace allocation failed */
+#define LTXATTN_ERR_SCRATCH     (-5) /* ltxattn_block_attention_noalloc: the call's split parts
+                                        need more than its static scratch */
 
 /* Attention kinds (index into ltxattn_block_io.attn). */
 enum {
@@ -160,6 +162,29 @@ int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void 
  * Errors: as ltxattn_block_attention. */
 int ltxattn_block_attention_overlap(ltxattn_handle *h, const ltxattn_block_io *io, void *hip_stream);
 
+/* The block call of ltxattn_block_attention without a handle and without
+ * allocating anything, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  cfg gives the device and the sizes the call is checked
+ * against, as for ltxattn_create.  The same kernels run in the same order on
+ * hip_stream and the outputs are bit-identical to ltxattn_block_attention's;
+ * the split parts of video self-attention's last round and of v2a go to a
+ * static scratch array of 64 MiB per device instead of a handle's workspace
+ * (each device the library runs on holds its copy until the process ends).
+ * A call needs (rows of split parts) x (head_dim + 2) x 4 bytes of it, at
+ * most 384 rows per compute unit: 51 MB at head_dim 128 on a 256-CU MI355X,
+ * so every request fits there; a request that would not fit is rejected
+ * with LTXATTN_ERR_SCRATCH before anything is enqueued.  Nothing in the
+ * scratch needs to start at zero: every part writes all its rows before the
+ * combine kernel reads them.  All calls on one device share its scratch, so
+ * calls whose work overlaps in time on one device (other streams, other
+ * threads) race and must be avoided.  No profiling events are recorded.
+ * The first call on a device sets it up (CU count, kernel attributes, the
+ * scratch's device address); later calls only plan and launch.
+ * Errors: INVALID_ARG, UNSUPPORTED (as ltxattn_block_attention), SCRATCH
+ * (all before any launch), HIP (see ltxattn_last_hip_error(NULL)). */
+int ltxattn_block_attention_noalloc(const ltxattn_config *cfg, const ltxattn_block_io *io, void *hip_stream);
+
 /* Validate a block call against a configuration without touching any
  * device: returns the status ltxattn_block_attention would return from its
  * checks on a 256-CU MI355X (LTXATTN_OK if the call would be launched): the
@@ -176,8 +201,8 @@ int ltxattn_destroy(ltxattn_handle *h);
 const char *ltxattn_status_string(int status);
 
 /* The hipError_t behind the last LTXATTN_ERR_HIP (or OOM) returned for
- * this handle; with h == NULL, that of the last failed ltxattn_create on
- * the calling thread.  0 if none. */
+ * this handle; with h == NULL, that of the last failed ltxattn_create or
+ * ltxattn_block_attention_noalloc on the calling thread.  0 if none. */
 int ltxattn_last_hip_error(const ltxattn_handle *h);
 
 /* Per-kind timing with HIP events recorded on the stream each kind runs on.

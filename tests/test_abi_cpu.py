@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings():
     assert lt.ltxattn_status_string(0) == "ok"
-    for s in (-1, -2, -3, -4):
+    for s in (-1, -2, -3, -4, -5):
         assert lt.ltxattn_status_string(s) not in ("ok", "unknown status")
     assert lt.ltxattn_status_string(7) == "unknown status"
 
@@ -63,6 +63,13 @@ def test_null_handles():
     assert lt._lib.ltxattn_profile_begin(None, 4) == lt.LTXATTN_ERR_INVALID_ARG
     assert lt._lib.ltxattn_profile_begin_kinds(None, 4, 1) == lt.LTXATTN_ERR_INVALID_ARG
     assert lt._lib.ltxattn_last_hip_error(None) == 0
+    assert lt._lib.ltxattn_block_attention_noalloc(None, ctypes.byref(io), None) == lt.LTXATTN_ERR_INVALID_ARG
+    cfg = lt.ltxattn_config(0, 4, 64, 1, 16, 16)
+    assert lt._lib.ltxattn_block_attention_noalloc(ctypes.byref(cfg), None, None) == lt.LTXATTN_ERR_INVALID_ARG
+    for bad, want in (((0, 4, 96, 1, 16, 16), lt.LTXATTN_ERR_UNSUPPORTED), ((0, 0, 64, 1, 16, 16), lt.LTXATTN_ERR_UNSUPPORTED),
+                      ((-1, 4, 64, 1, 16, 16), lt.LTXATTN_ERR_INVALID_ARG), ((0, 4, 64, 0, 16, 16), lt.LTXATTN_ERR_INVALID_ARG)):
+        cfg = lt.ltxattn_config(*bad)
+        assert lt._lib.ltxattn_block_attention_noalloc(ctypes.byref(cfg), ctypes.byref(io), None) == want, bad
 
 
 # ------------------------------------------------------------ block checks

@@ -70,6 +70,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "ltxattn.h"
 
@@ -1484,21 +1485,46 @@ struct DeviceGuard {
     }
 };
 
-// hipError_t of the last failed ltxattn_create on this thread (no handle to keep it in).
+// hipError_t of the last failed call without a handle to keep it in
+// (ltxattn_create, ltxattn_block_attention_noalloc) on this thread.
 thread_local int g_create_hip_error = 0;
 
 int hip_fail(ltxattn_handle *h, hipError_t e) {
     if (h) h->last_hip_error = (int)e;
+    else g_create_hip_error = (int)e;
     return LTXATTN_ERR_HIP;
+}
+
+// Kernels that take more dynamic LDS than the default limit: the resident-key
+// kernel keeps up to RESIDENT_KV_MAX keys of K and V (and, staged, the Q/O row
+// slots) in LDS, the ring kernels four K/V tile pairs.  For the current device.
+hipError_t set_kernel_lds_limits() {
+    const void *kvres[8] = {
+        (const void *)&fa_kvres_kernel<128, 8, true, false>, (const void *)&fa_kvres_kernel<128, 8, true, true>,
+        (const void *)&fa_kvres_kernel<128, 8, false, false>, (const void *)&fa_kvres_kernel<128, 8, false, true>,
+        (const void *)&fa_kvres_kernel<128, 4, false, false>, (const void *)&fa_kvres_kernel<128, 4, false, true>,
+        (const void *)&fa_kvres_kernel<64, 4, false, false>, (const void *)&fa_kvres_kernel<64, 4, false, true>};
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 8 && e == hipSuccess; ++i)
+        e = hipFuncSetAttribute(kvres[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)&fa_ring_kernel<128, RING_NW, 2>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 128 * 2);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)&fa_ring_kernel<64, RING_NW, 2>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 64 * 2);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void *)&fa_ring_kernel<128, RING_NW, 1>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 128 * 2);
+    return e;
 }
 
 // Launch one planned kind on stream st, with its split parts (if any) in
 // its region of ws, then the combine kernel that merges them.  When
 // `after_main` is given and a combine kernel follows, the event is recorded
 // between the two and *mid_recorded is set.
-int launch_plan(ltxattn_handle *h, const Plan &p, const Workspace &ws, hipStream_t st, hipEvent_t after_main,
+int launch_plan(ltxattn_handle *h, int D, const Plan &p, const Workspace &ws, hipStream_t st, hipEvent_t after_main,
                 bool *mid_recorded) {
-    const int D = h->head_dim;
     FaArgs a = p.a;
     if (p.region != REGION_NONE) {
         const int64_t r0 = p.region == REGION_V2A ? ws.rows[REGION_TAIL] : 0;
@@ -1591,7 +1617,8 @@ int enqueue_block(ltxattn_handle *h, const ltxattn_block_io *io, hipStream_t st,
         if (e != hipSuccess) return hip_fail(h, e);
         if (!on[k]) continue;
         bool mid_rec = false;
-        const int rc = launch_plan(h, plans[k], h->ws, ks, rec_k ? ev[n_ev] : nullptr, rec_k ? &mid_rec : nullptr);
+        const int rc = launch_plan(h, h->head_dim, plans[k], h->ws, ks, rec_k ? ev[n_ev] : nullptr,
+                                   rec_k ? &mid_rec : nullptr);
         if (rc) return rc;
         if (rec_k) {
             if (mid_rec) pc->mid[k] = (int8_t)n_ev++;
@@ -1629,6 +1656,48 @@ hipError_t release(ltxattn_handle *h) {
 
 }  // namespace
 
+// ------------------------------------------------- allocation-free block call
+// ltxattn_block_attention_noalloc keeps its split parts in this file-scope
+// device array instead of a handle's workspace.  Each device holds its own
+// copy from the library's first use on it until the process ends.  In host
+// code `scratch` only stands in for the symbol: its address on a device comes
+// from hipGetSymbolAddress, taken once per device at that device's set-up.
+constexpr int64_t SCRATCH_BYTES = (int64_t)64 << 20;
+static __device__ __align__(256) float scratch[SCRATCH_BYTES / 4];
+
+namespace {
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
+struct NoallocDevice {
+    float *scratch;   // this device's copy of `scratch`; null until set up
+    int num_cus;
+};
+std::mutex g_noalloc_mutex;
+NoallocDevice g_noalloc[NOALLOC_MAX_DEVICES];
+
+// Set-up of the current device, once: its CU count, the kernels' LDS limits
+// and the device address of `scratch`.
+int noalloc_device(int device, NoallocDevice *out) {
+    std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+    NoallocDevice &d = g_noalloc[device];
+    if (!d.scratch) {
+        int num_cus = 0;
+        hipError_t e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, device);
+        if (e == hipSuccess) e = set_kernel_lds_limits();
+        void *ptr = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e == hipSuccess && !ptr) e = hipErrorInvalidSymbol;
+        if (e != hipSuccess) return hip_fail(nullptr, e);
+        d.num_cus = num_cus;
+        d.scratch = (float *)ptr;
+    }
+    *out = d;
+    return LTXATTN_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *ltxattn_status_string(int status) {
@@ -1638,6 +1707,7 @@ const char *ltxattn_status_string(int status) {
         case LTXATTN_ERR_UNSUPPORTED: return "unsupported configuration";
         case LTXATTN_ERR_HIP: return "HIP runtime error";
         case LTXATTN_ERR_OOM: return "device workspace allocation failed";
+        case LTXATTN_ERR_SCRATCH: return "split parts need more than the static scratch of the allocation-free call";
         default: return "unknown status";
     }
 }
@@ -1668,26 +1738,7 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
     if (g.err != hipSuccess) { g_create_hip_error = (int)g.err; free(h); return LTXATTN_ERR_HIP; }
     e = hipDeviceGetAttribute(&h->num_cus, hipDeviceAttributeMultiprocessorCount, h->device);
     if (e != hipSuccess) { g_create_hip_error = (int)e; free(h); return LTXATTN_ERR_HIP; }
-    // The resident-key kernel keeps up to RESIDENT_KV_MAX keys of K and V (and,
-    // staged, the Q/O row slots) in LDS: allow it all of a CU's LDS.
-    {
-        const void *kvres[8] = {
-            (const void *)&fa_kvres_kernel<128, 8, true, false>, (const void *)&fa_kvres_kernel<128, 8, true, true>,
-            (const void *)&fa_kvres_kernel<128, 8, false, false>, (const void *)&fa_kvres_kernel<128, 8, false, true>,
-            (const void *)&fa_kvres_kernel<128, 4, false, false>, (const void *)&fa_kvres_kernel<128, 4, false, true>,
-            (const void *)&fa_kvres_kernel<64, 4, false, false>, (const void *)&fa_kvres_kernel<64, 4, false, true>};
-        for (int i = 0; i < 8 && e == hipSuccess; ++i)
-            e = hipFuncSetAttribute(kvres[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
-    }
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_ring_kernel<128, RING_NW, 2>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 128 * 2);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_ring_kernel<64, RING_NW, 2>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 64 * 2);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_ring_kernel<128, RING_NW, 1>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 128 * 2);
+    e = set_kernel_lds_limits();
     if (e != hipSuccess) { g_create_hip_error = (int)e; free(h); return LTXATTN_ERR_HIP; }
     // Workspace of the split items: both regions at their bounds for this
     // device's compute units.
@@ -1734,6 +1785,43 @@ int ltxattn_block_attention(ltxattn_handle *h, const ltxattn_block_io *io, void 
 
 int ltxattn_block_attention_overlap(ltxattn_handle *h, const ltxattn_block_io *io, void *hip_stream) {
     return enqueue_block(h, io, (hipStream_t)hip_stream, true);
+}
+
+int ltxattn_block_attention_noalloc(const ltxattn_config *cfg, const ltxattn_block_io *io, void *hip_stream) {
+    if (!cfg || !io) return LTXATTN_ERR_INVALID_ARG;
+    if (cfg->head_dim != 64 && cfg->head_dim != 128) return LTXATTN_ERR_UNSUPPORTED;
+    if (cfg->heads < 1) return LTXATTN_ERR_UNSUPPORTED;
+    if (cfg->max_batch < 1 || cfg->max_video_len < 1 || cfg->max_audio_len < 1 || cfg->device < 0 ||
+        cfg->device >= NOALLOC_MAX_DEVICES)
+        return LTXATTN_ERR_INVALID_ARG;
+    int ndev = 0;
+    hipError_t e = hipGetDeviceCount(&ndev);
+    if (e != hipSuccess) return hip_fail(nullptr, e);
+    if (cfg->device >= ndev) return LTXATTN_ERR_INVALID_ARG;
+    DeviceGuard g(cfg->device);
+    if (g.err != hipSuccess) return hip_fail(nullptr, g.err);
+    NoallocDevice dev;
+    int rc = noalloc_device(cfg->device, &dev);
+    if (rc) return rc;
+    bool on[4];
+    if ((rc = validate_block(*cfg, io, dev.num_cus, on))) return rc;
+    Plan plans[4];
+    plan_block(*cfg, io, on, dev.num_cus, plans);
+    // The scratch holds exactly the regions this call uses: TAIL then V2A.
+    Workspace ws = {};
+    for (int k = 0; k < 4; ++k)
+        if (on[k] && plans[k].region != REGION_NONE) ws.rows[plans[k].region] = plans[k].ws_rows;
+    const int64_t rows = ws.rows[REGION_TAIL] + ws.rows[REGION_V2A];
+    if (rows * (cfg->head_dim + 2) * (int64_t)sizeof(float) > SCRATCH_BYTES) return LTXATTN_ERR_SCRATCH;
+    ws.o = dev.scratch;
+    ws.ml = dev.scratch + rows * cfg->head_dim;
+    for (int n = 0; n < 4; ++n) {
+        const int k = KIND_ORDER[n];
+        if (!on[k]) continue;
+        if ((rc = launch_plan(nullptr, cfg->head_dim, plans[k], ws, (hipStream_t)hip_stream, nullptr, nullptr)))
+            return rc;
+    }
+    return LTXATTN_OK;
 }
 
 int ltxattn_profile_begin(ltxattn_handle *h, int32_t max_calls) {

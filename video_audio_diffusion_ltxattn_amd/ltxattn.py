@@ -28,6 +28,7 @@ LTXATTN_ERR_INVALID_ARG = -1
 LTXATTN_ERR_UNSUPPORTED = -2
 LTXATTN_ERR_HIP = -3
 LTXATTN_ERR_OOM = -4
+LTXATTN_ERR_SCRATCH = -5
 
 LTXATTN_VIDEO_SELF = 0
 LTXATTN_AUDIO_SELF = 1
@@ -82,6 +83,8 @@ def _load():
         "ltxattn_create": ([ctypes.POINTER(ltxattn_config), ctypes.POINTER(P)], ctypes.c_int),
         "ltxattn_block_attention": ([P, ctypes.POINTER(ltxattn_block_io), P], ctypes.c_int),
         "ltxattn_block_attention_overlap": ([P, ctypes.POINTER(ltxattn_block_io), P], ctypes.c_int),
+        "ltxattn_block_attention_noalloc": ([ctypes.POINTER(ltxattn_config), ctypes.POINTER(ltxattn_block_io), P],
+                                            ctypes.c_int),
         "ltxattn_check_block": ([ctypes.POINTER(ltxattn_config), ctypes.POINTER(ltxattn_block_io)],
                                 ctypes.c_int),
         "ltxattn_destroy": ([P], ctypes.c_int),
@@ -102,6 +105,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("ltxattn_create", "ltxattn_block_attention", "ltxattn_block_attention_overlap",
+            "ltxattn_block_attention_noalloc",
             "ltxattn_check_block",
             "ltxattn_destroy", "ltxattn_status_string", "ltxattn_last_hip_error",
             "ltxattn_profile_begin", "ltxattn_profile_begin_kinds", "ltxattn_profile_read",
@@ -133,6 +137,13 @@ def ltxattn_block_attention_overlap(h, io: ltxattn_block_io, stream: int) -> Non
     if rc != LTXATTN_OK:
         raise LtxattnError(rc, "ltxattn_block_attention_overlap",
                            _lib.ltxattn_last_hip_error(h) if rc == LTXATTN_ERR_HIP else 0)
+
+
+def ltxattn_block_attention_noalloc(cfg: ltxattn_config, io: ltxattn_block_io, stream: int) -> None:
+    rc = _lib.ltxattn_block_attention_noalloc(ctypes.byref(cfg), ctypes.byref(io), ctypes.c_void_p(stream))
+    if rc != LTXATTN_OK:
+        raise LtxattnError(rc, "ltxattn_block_attention_noalloc",
+                           _lib.ltxattn_last_hip_error(None) if rc == LTXATTN_ERR_HIP else 0)
 
 
 def ltxattn_check_block(cfg: ltxattn_config, io: ltxattn_block_io) -> int:
