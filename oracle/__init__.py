@@ -22,11 +22,19 @@ v2a           audio      video       all video tokens
 Audio keys at or beyond ``audio_kv_len`` are padding (the audio stream is
 padded, same PR, "Description") and get weight exactly zero.
 
-Gated attention (named among the DiT's parts by TensorRT-Model-Connect PR
-#1586, the commit onboarding LTX-2.5, which gives no gate formula): an
-optional gate of the output's shape, taken as given (already activated), is
-multiplied elementwise into each output row: o_gated[b, i, h, d] =
-gate[b, i, h, d] * o[b, i, h, d].
+Two optional per-kind steps, both computed in the C file too:
+
+* gated attention (named among the DiT's parts by TensorRT-Model-Connect PR
+  #1586, the commit onboarding LTX-2.5, which gives no gate formula): a gate
+  of the output's shape, taken as given (already activated), multiplies the
+  output elementwise;
+* the QK-norm + rotary prologue (the same commit: keys are normed and
+  rotated before the context-parallel gather, with fp32 norm and RoPE
+  islands in a bf16 network): ``qk_prologue`` -- per-(token, head) RMS norm
+  with a per-channel weight, then a rotation of channel pairs by the
+  caller's per-position cos/sin tables, rounded to the bf16 the attention
+  reads.  ``block_attention(prologues=...)`` applies it to a kind's Q and K
+  before the attention.
 """
 
 from __future__ import annotations
@@ -62,12 +70,15 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         p = ctypes.c_void_p
         i64 = ctypes.c_int64
-        lib.ltxattn_oracle_attention.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64,
+        lib.ltxattn_oracle_attention.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64,
                                                  p, p, ctypes.c_int]
         lib.ltxattn_oracle_attention.restype = ctypes.c_int
-        lib.ltxattn_oracle_attention_rows.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64,
+        lib.ltxattn_oracle_attention_rows.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64,
                                                       p, i64, p, p, ctypes.c_int]
         lib.ltxattn_oracle_attention_rows.restype = ctypes.c_int
+        lib.ltxattn_oracle_qk_prologue.argtypes = [p, i64, i64, i64, i64, p, p, p, ctypes.c_double,
+                                                   ctypes.c_int, p, p]
+        lib.ltxattn_oracle_qk_prologue.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -111,10 +122,13 @@ def _shapes(q, k, v, kv_len):
 
 
 def _gate(gate, shape):
-    g = _as_f32(gate).astype(np.float64)
+    """The gate as float32 values of the output's shape, or None."""
+    if gate is None:
+        return None
+    g = _as_f32(gate)
     if g.shape != shape:
         raise ValueError(f"gate shape {g.shape}, expected {shape}")
-    return g
+    return np.ascontiguousarray(g)
 
 
 def attention(q, k, v, kv_len=None, threads=None, return_lse=False, gate=None):
@@ -127,16 +141,15 @@ def attention(q, k, v, kv_len=None, threads=None, return_lse=False, gate=None):
     """
     q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
     B, Sq, Sk, L, H, D = _shapes(q, k, v, kv_len)
+    g = _gate(gate, (B, Sq, H, D))
     out = np.empty((B, Sq, H, D), dtype=np.float64)
     lse = np.empty((B, Sq, H), dtype=np.float64) if return_lse else None
     rc = _load().ltxattn_oracle_attention(
-        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, Sq, Sk, L, H, D,
-        out.ctypes.data, lse.ctypes.data if lse is not None else None,
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, g.ctypes.data if g is not None else None,
+        B, Sq, Sk, L, H, D, out.ctypes.data, lse.ctypes.data if lse is not None else None,
         threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle failed with {rc}")
-    if gate is not None:
-        out *= _gate(gate, out.shape)
     return (out, lse) if return_lse else out
 
 
@@ -147,20 +160,55 @@ def attention_rows(q, k, v, rows, kv_len=None, threads=None, return_lse=False, g
     """
     q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
     B, Sq, Sk, L, H, D = _shapes(q, k, v, kv_len)
+    g = _gate(gate, (B, Sq, H, D))
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
     n = rows.shape[0]
     out = np.empty((n, D), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64) if return_lse else None
     rc = _load().ltxattn_oracle_attention_rows(
-        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, Sq, Sk, L, H, D,
-        rows.ctypes.data, n, out.ctypes.data,
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, g.ctypes.data if g is not None else None,
+        B, Sq, Sk, L, H, D, rows.ctypes.data, n, out.ctypes.data,
         lse.ctypes.data if lse is not None else None, threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle failed with {rc}")
-    if gate is not None:
-        g = _gate(gate, (B, Sq, H, D))
-        out *= g[rows[:, 0], rows[:, 2], rows[:, 1]]
     return (out, lse) if return_lse else out
+
+
+PAIRINGS = {"half": 0, "interleaved": 1}
+
+
+def qk_prologue(x, weight, cos, sin, eps, pairing="half", round_bf16=True):
+    """RMS norm of every (token, head) row of x [B, S, H, D] over its D
+    channels with the per-channel weight [D], then the rotation of channel
+    pairs by cos/sin [S, D/2] of the row's token; pairing "half" pairs
+    channels i and i + D/2, "interleaved" 2i and 2i + 1.  Returns the bf16
+    bits (uint16) the attention reads, or with round_bf16=False the float64
+    values before rounding."""
+    x = _as_f32(x)
+    if x.ndim != 4:
+        raise ValueError("x must be [B, S, H, D]")
+    B, S, H, D = x.shape
+    w = np.ascontiguousarray(_as_f32(weight).reshape(-1))
+    c = np.ascontiguousarray(_as_f32(cos))
+    s = np.ascontiguousarray(_as_f32(sin))
+    if w.shape != (D,) or c.shape != (S, D // 2) or s.shape != (S, D // 2):
+        raise ValueError(f"weight {w.shape}, cos {c.shape}, sin {s.shape} for x {x.shape}")
+    out = np.empty(x.shape, np.float64) if not round_bf16 else None
+    bits = np.empty(x.shape, np.uint16) if round_bf16 else None
+    rc = _load().ltxattn_oracle_qk_prologue(
+        x.ctypes.data, B, S, H, D, w.ctypes.data, c.ctypes.data, s.ctypes.data, float(eps),
+        PAIRINGS[pairing], out.ctypes.data if out is not None else None,
+        bits.ctypes.data if bits is not None else None)
+    if rc != 0:
+        raise RuntimeError(f"oracle prologue failed with {rc}")
+    return bits if round_bf16 else out
+
+
+def apply_prologue(q, k, pro):
+    """(q, k) of one attention after its prologue: pro holds q_weight,
+    k_weight, q_cos, q_sin, k_cos, k_sin, eps and pairing."""
+    return (qk_prologue(q, pro["q_weight"], pro["q_cos"], pro["q_sin"], pro["eps"], pro["pairing"]),
+            qk_prologue(k, pro["k_weight"], pro["k_cos"], pro["k_sin"], pro["eps"], pro["pairing"]))
 
 
 def pairing(kind: str, inputs: dict, audio_kv_len: int):
@@ -178,21 +226,28 @@ def pairing(kind: str, inputs: dict, audio_kv_len: int):
     raise ValueError(kind)
 
 
-def block_attention(inputs: dict, audio_kv_len: int, kinds=KINDS, threads=None, gates=None):
+def block_attention(inputs: dict, audio_kv_len: int, kinds=KINDS, threads=None, gates=None,
+                    prologues=None):
     """All four attentions of one block; returns {kind: o float64 [B, Sq, H, D]}.
-    gates: optional {kind: gate [B, Sq, H, D]}."""
+    gates: optional {kind: gate [B, Sq, H, D]}; prologues: optional {kind:
+    QK-norm + rotary parameters (see apply_prologue)}."""
     out = {}
     for kind in kinds:
         q, k, v, L = pairing(kind, inputs, audio_kv_len)
+        if prologues and kind in prologues:
+            q, k = apply_prologue(q, k, prologues[kind])
         out[kind] = attention(q, k, v, kv_len=L, threads=threads, gate=(gates or {}).get(kind))
     return out
 
 
-def block_attention_rows(inputs: dict, audio_kv_len: int, rows: dict, threads=None, gates=None):
+def block_attention_rows(inputs: dict, audio_kv_len: int, rows: dict, threads=None, gates=None,
+                         prologues=None):
     """Selected rows of each attention: rows = {kind: int array [n, 3] of (b, h, i)};
-    gates: optional {kind: gate [B, Sq, H, D]}."""
+    gates and prologues as for block_attention."""
     out = {}
     for kind, r in rows.items():
         q, k, v, L = pairing(kind, inputs, audio_kv_len)
+        if prologues and kind in prologues:
+            q, k = apply_prologue(q, k, prologues[kind])
         out[kind] = attention_rows(q, k, v, r, kv_len=L, threads=threads, gate=(gates or {}).get(kind))
     return out
