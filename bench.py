@@ -120,6 +120,71 @@ def cpu_baseline(inputs: dict, w: synth.Workload, min_s: float, max_s: float) ->
     }
 
 
+def torch_prologue(x, w, cos, sin, eps, pairing):
+    """The QK-norm + rotary prologue as separate torch operations in fp32 (the
+    unfused passes a caller would otherwise run before the block call), for
+    comparison only."""
+    import torch
+    P = x.shape[-1] // 2
+    xf = x.float()
+    y = xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + eps) * w
+    ya, yc = (y[..., :P], y[..., P:]) if pairing == "half" else (y[..., 0::2], y[..., 1::2])
+    c, s = cos[None, :, None, :], sin[None, :, None, :]
+    za, zc = ya * c - yc * s, ya * s + yc * c
+    z = torch.cat([za, zc], -1) if pairing == "half" else torch.stack([za, zc], -1).flatten(-2)
+    return z.to(torch.bfloat16)
+
+
+def prologue_comparison(lt, ba, dev, outs, w, dpros, stream, calls):
+    """Block time with the prologue fused (query loads + one pass per distinct
+    keys), against the same attention after separate torch passes over every
+    kind's queries and keys, and against the block with no prologue."""
+    import torch
+    q_of = {"video_self": "video_q", "audio_self": "audio_q", "a2v": "video_q", "v2a": "audio_q"}
+    k_of = {"video_self": "video_k", "audio_self": "audio_k", "a2v": "audio_k", "v2a": "video_k"}
+    v_of = {"video_self": "video_v", "audio_self": "audio_v", "a2v": "audio_v", "v2a": "video_v"}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(calls):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / calls
+
+    io_fused = ba.make_io(dev, w.audio_kv_len, outs, prologues=dpros)
+    io_plain = ba.make_io(dev, w.audio_kv_len, outs)
+    fused = timed(lambda: lt.ltxattn_block_attention(ba.handle, io_fused, stream.cuda_stream))
+    plain = timed(lambda: lt.ltxattn_block_attention(ba.handle, io_plain, stream.cuda_stream))
+    keep = {}
+
+    def unfused():
+        ins = {}
+        done = {}
+        for k in outs:
+            p = dpros[k]
+            kk = (k_of[k], id(p["k_weight"]))
+            if kk not in done:
+                done[kk] = torch_prologue(dev[k_of[k]], p["k_weight"], p["k_cos"], p["k_sin"], p["eps"], p["pairing"])
+            q = torch_prologue(dev[q_of[k]], p["q_weight"], p["q_cos"], p["q_sin"], p["eps"], p["pairing"])
+            ins[k] = (q, done[kk], dev[v_of[k]])
+        keep["io"] = ba.make_io(dev, w.audio_kv_len, outs, inputs=ins)
+        keep["ins"] = ins
+        lt.ltxattn_block_attention(ba.handle, keep["io"], stream.cuda_stream)
+    unfused_ms = timed(unfused)
+    return {"fused_block_ms": round(fused, 4), "unfused_torch_block_ms": round(unfused_ms, 4),
+            "plain_block_ms": round(plain, 4),
+            "fused_overhead_ms": round(fused - plain, 4), "unfused_overhead_ms": round(unfused_ms - plain, 4),
+            "pairing": next(iter(dpros.values()))["pairing"],
+            "note": "prologue on every kind: per-kind q weights, k weights shared by the kinds that read "
+                    "the same keys (one key pass per stream); unfused = torch fp32 ops per tensor, then the "
+                    "plain block on their bf16 outputs"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +201,9 @@ def main():
     ap.add_argument("--gated", action="store_true",
                     help="gated attention: every kind's output multiplied by a gate of its shape "
                          "(uniform in (0, 1), bf16)")
+    ap.add_argument("--qknorm-rope", action="store_true",
+                    help="QK-norm + rotary prologue on every kind (raw Q/K in, normed and rotated inside); "
+                         "also times the same attention after unfused torch passes")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write this many MiB of scratch between block calls (past the last-level "
                          "cache); value then comes from the library's per-call events")
@@ -170,7 +238,7 @@ def main():
     dev = {}
     for n, a in inputs.items():
         dev[n] = torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to("cuda:0")
-    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len, qk_prologue=args.qknorm_rope)
     outs = {k: torch.empty_like(dev["video_q"] if k in ("video_self", "a2v") else dev["audio_q"])
             for k in KINDS}
     stream = torch.cuda.current_stream()
@@ -183,7 +251,12 @@ def main():
     if args.gated:
         gates = {k: (torch.rand_like(outs[k], dtype=torch.float32) * 0.999 + 0.0005).to(torch.bfloat16)
                  for k in KINDS}
-    io = ba.make_io(dev, w.audio_kv_len, outs, kind_inputs, gates)
+    dpros = None
+    if args.qknorm_rope:
+        pros = synth.make_prologues(w, "half", shared_k=True)
+        dpros = {k: {n: (torch.from_numpy(v).to("cuda:0") if isinstance(v, np.ndarray) else v)
+                     for n, v in p.items()} for k, p in pros.items()}
+    io = ba.make_io(dev, w.audio_kv_len, outs, kind_inputs, gates, dpros)
     scratch = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device="cuda:0")
                if args.flush_mib else None)
 
@@ -273,6 +346,7 @@ def main():
                  "schedule": "overlap" if args.overlap else "sequential",
                  "inputs": "distinct per kind" if args.distinct else "two stream triples",
                  "output_gate": bool(args.gated),
+                 "qk_prologue": bool(args.qknorm_rope),
                  "flush_mib_between_calls": args.flush_mib},
         "kinds": kinds,
         "roofline": {"kernel": video_kernel_name(w),
@@ -282,6 +356,8 @@ def main():
                      "traffic": measured_traffic(w),
                      "avg_launch_ms": round(vs_ms, 5)},
     }
+    if args.qknorm_rope:
+        out["qknorm_rope"] = prologue_comparison(lt, ba, dev, outs, w, dpros, stream, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inputs, w, args.cpu_seconds, 3 * args.cpu_seconds)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)

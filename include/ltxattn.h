@@ -17,9 +17,11 @@
  * multiple of the sequence-parallel degree), so the caller passes the
  * number of valid audio keys; audio key rows at or beyond it get weight
  * exactly zero and are never read.  Padded audio query rows are computed
- * like any other row.  Q and K arrive already normalised and rotary-embedded
- * (the context-parallel DiT of TensorRT-Model-Connect PR #1586 all-gathers
- * keys after those steps), so no norm or RoPE happens here.
+ * like any other row.  Q and K arrive normalised and rotary-embedded (the
+ * context-parallel DiT of TensorRT-Model-Connect PR #1586 all-gathers keys
+ * after those steps); a caller may instead hand over the raw Q and K with
+ * the parameters of those two steps (ltxattn_qk_prologue), and the library
+ * applies them on the way in.
  *
  * Precision: bf16 inputs and outputs with fp32 accumulation and fp32
  * softmax statistics (the DiT of PR #1586 keeps the network in bf16 with
@@ -56,7 +58,8 @@ extern "C" {
                                         output overlapping another tensor */
 #define LTXATTN_ERR_UNSUPPORTED (-2) /* head_dim not 64 or 128, heads < 1, tensor too large
                                         for 32-bit buffer offsets, split parts that would not
-                                        fit the workspace */
+                                        fit the workspace, a prologue on a handle created
+                                        without its workspace (or on the allocation-free call) */
 #define LTXATTN_ERR_HIP         (-3) /* a HIP call or kernel launch failed; see
                                         ltxattn_last_hip_error */
 #define LTXATTN_ERR_OOM         (-4) /* device workspace allocation failed */
@@ -87,6 +90,10 @@ typedef struct {
     int32_t max_batch;     /* >= 1 */
     int32_t max_video_len; /* >= 1, video tokens */
     int32_t max_audio_len; /* >= 1, audio buffer rows (padded length) */
+    int32_t qk_prologue;   /* 1: the handle also holds the workspace of the keys of the
+                              QK-norm + rotary prologue (two video-sized and two
+                              audio-sized bf16 key tensors at the capacities); 0: calls
+                              with a prologue are refused */
 } ltxattn_config;
 
 /* One bf16 tensor [B, S, H, D], D contiguous.  data is a device pointer,
@@ -98,6 +105,40 @@ typedef struct {
     int64_t stride_b, stride_s, stride_h;
 } ltxattn_tensor;
 
+/* Rotary pairings of the QK-norm + rotary prologue. */
+enum {
+    LTXATTN_ROPE_HALF = 0,        /* channel i pairs with channel i + D/2 */
+    LTXATTN_ROPE_INTERLEAVED = 1  /* channel 2i pairs with channel 2i + 1 */
+};
+
+/* Optional QK-norm + rotary prologue of one attention (q_weight == NULL:
+ * none; the keys and queries of the joint DiT are normed and rotated before
+ * attention, with fp32 norm and RoPE islands in a bf16 network, PR #1586,
+ * the commit onboarding LTX-2.5; its RoPE tables are data per latent grid,
+ * same PR, "The DiT plan serves both grids").  The pages give no formulas;
+ * what is computed, for every (batch, token s, head) row x of q (and of k,
+ * with the k parameters):
+ *   r   = 1 / sqrt(mean over the D channels of x^2 + eps)
+ *   y_d = x_d * r * weight[d]                     (RMS norm, per head)
+ *   for every pair i < D/2 of channels (a, c):
+ *     out_a = y_a * cos[s][i] - y_c * sin[s][i]
+ *     out_c = y_a * sin[s][i] + y_c * cos[s][i]   (rotation)
+ * in fp32, rounded to bf16 before the attention reads it.  The weights are
+ * fp32 [D]; the tables fp32 [rows][D/2], row-major, one row per token of
+ * that tensor (every buffer row: video_len or audio_len rows); all six
+ * pointers are device pointers, 16-byte aligned, and must be given when
+ * q_weight is.  eps > 0.  Q is normed and rotated as the attention kernels
+ * load it; K by a pass that writes the prepared keys into the handle's
+ * workspace (kinds that name the same K tensor and the same k parameters
+ * share that pass). */
+typedef struct {
+    const float *q_weight, *k_weight;
+    const float *q_cos, *q_sin;
+    const float *k_cos, *k_sin;
+    float eps;
+    int32_t pairing;   /* LTXATTN_ROPE_HALF or LTXATTN_ROPE_INTERLEAVED */
+} ltxattn_qk_prologue;
+
 /* One attention's tensors.  gate is optional (gate.data == NULL: none):
  * a per-channel output gate of o's shape and layout rules, bf16; when given,
  * o = gate * softmax(Q K^T / sqrt(D)) V elementwise, the product taken in
@@ -107,6 +148,7 @@ typedef struct {
 typedef struct {
     ltxattn_tensor q, k, v, o;
     ltxattn_tensor gate;
+    ltxattn_qk_prologue prologue;
 } ltxattn_attn_io;
 
 /* One block call.  Row counts by kind:
@@ -179,6 +221,8 @@ int ltxattn_block_attention_overlap(ltxattn_handle *h, const ltxattn_block_io *i
  * combine kernel reads them.  All calls on one device share its scratch, so
  * calls whose work overlaps in time on one device (other streams, other
  * threads) race and must be avoided.  No profiling events are recorded.
+ * The QK-norm + rotary prologue is not available here (its keys need a
+ * workspace): a call with one is refused with LTXATTN_ERR_UNSUPPORTED.
  * The first call on a device sets it up (CU count, kernel attributes, the
  * scratch's device address); later calls only plan and launch.
  * Errors: INVALID_ARG, UNSUPPORTED (as ltxattn_block_attention), SCRATCH

@@ -244,6 +244,7 @@ def test_struct_layouts_match_the_header(tmp_path):
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     fields = {"ltxattn_config": [f for f, _ in lt.ltxattn_config._fields_],
               "ltxattn_tensor": [f for f, _ in lt.ltxattn_tensor._fields_],
+              "ltxattn_qk_prologue": [f for f, _ in lt.ltxattn_qk_prologue._fields_],
               "ltxattn_attn_io": [f for f, _ in lt.ltxattn_attn_io._fields_],
               "ltxattn_block_io": [f for f, _ in lt.ltxattn_block_io._fields_]}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "ltxattn.h"', "int main(void) {"]
@@ -335,3 +336,51 @@ def test_split_parts_fit_the_workspace_at_any_size():
         io.attn[3] = lt.ltxattn_attn_io(aq, vk, vv, t(9, La_))
         cfg = lt.ltxattn_config(0, H_, D_, B_, Sv_, La_)
         assert lt.ltxattn_check_block(cfg, io) == lt.LTXATTN_OK, (B_, H_, D_, Sv_, La_, Lk_)
+
+
+# ------------------------------------------- QK-norm + rotary prologue
+def _prologue(base=1 << 41):
+    """A prologue whose six arrays are 16-byte aligned fake addresses."""
+    return lt.ltxattn_qk_prologue(base, base + 4096, base + 8192, base + 12288, base + 16384, base + 20480,
+                                  1e-6, lt.LTXATTN_ROPE_HALF)
+
+
+CFG_PRO = lt.ltxattn_config(0, H, D, B, Sv, La, 1)
+
+
+def test_prologue_accepted_with_workspace_only():
+    io = make_io()
+    for k in range(4):
+        io.attn[k].prologue = _prologue()
+    assert check(io, CFG_PRO) == lt.LTXATTN_OK
+    assert check(io, CFG) == lt.LTXATTN_ERR_UNSUPPORTED        # handle without the key workspace
+    io.attn[2].prologue = lt.ltxattn_qk_prologue()             # q_weight NULL: no prologue for a2v
+    assert check(io, CFG_PRO) == lt.LTXATTN_OK
+
+
+@pytest.mark.parametrize("kind", range(4))
+@pytest.mark.parametrize("mutate", ["null", "misaligned", "eps_zero", "eps_negative", "eps_inf", "eps_nan",
+                                    "pairing"])
+def test_bad_prologue(kind, mutate):
+    fields = ["k_weight", "q_cos", "q_sin", "k_cos", "k_sin"]
+    cases = []
+    if mutate in ("null", "misaligned"):
+        for f in fields:
+            p = _prologue()
+            setattr(p, f, None if mutate == "null" else getattr(p, f) + 4)
+            cases.append(p)
+        if mutate == "misaligned":
+            p = _prologue()
+            p.q_weight += 8
+            cases.append(p)
+    else:
+        p = _prologue()
+        if mutate == "pairing":
+            p.pairing = 2
+        else:
+            p.eps = {"eps_zero": 0.0, "eps_negative": -1e-6, "eps_inf": float("inf"), "eps_nan": float("nan")}[mutate]
+        cases.append(p)
+    for p in cases:
+        io = make_io()
+        io.attn[kind].prologue = p
+        assert check(io, CFG_PRO) == lt.LTXATTN_ERR_INVALID_ARG, (kind, mutate)

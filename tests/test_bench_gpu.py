@@ -38,7 +38,11 @@ def test_bench_json_line():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("flag", ["--overlap", "--distinct", "--gated"])
+@pytest.mark.parametrize("flag", ["--overlap", "--distinct", "--gated", "--qknorm-rope"])
 def test_bench_modes(flag):
     d = run_bench("--no-cpu-baseline", flag)
     assert d["value"] > 0 and "cpu_baseline" not in d
+    if flag == "--qknorm-rope":
+        p = d["qknorm_rope"]
+        assert d["config"]["qk_prologue"] is True
+        assert p["fused_block_ms"] > 0 and p["unfused_torch_block_ms"] > 0 and p["plain_block_ms"] > 0

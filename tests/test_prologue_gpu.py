@@ -1,0 +1,165 @@
+"""The QK-norm + rotary prologue on the GPU against the oracle, through the
+C ABI: raw Q and K go in with per-kind norm weights and rotary tables, the
+library normalises and rotates Q as its attention kernels load it and K in a
+pass of its own, and every output must match the oracle's prologue followed
+by its attention (max-abs 2e-2, mean-abs 2e-3, rel-L2 1e-2, cos 0.9999).
+
+Every attention kernel's prologue path is reached: the 256-query ring kernel
+(video self-attention), the two-key-group ring at D = 128 and 64 (v2a), the
+two-buffer kernel at D = 128 and 64, the resident-key kernel staged and
+unstaged at 8 and 4 waves and at D = 64 (a2v, audio self-attention), gated and
+ungated; both pairings; kinds that share their keys' pass and kinds that do
+not; the concurrent call."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import compare, log, to_device, to_numpy
+from video_audio_diffusion_ltxattn_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ("video_self", "audio_self", "a2v", "v2a")
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _torch
+    if not _torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    return _torch
+
+
+@pytest.fixture(scope="module")
+def lt(torch):
+    from video_audio_diffusion_ltxattn_amd import ltxattn
+    return ltxattn
+
+
+def dev_prologues(torch, pros):
+    return {k: {n: (torch.from_numpy(v).to("cuda:0") if isinstance(v, np.ndarray) else v) for n, v in p.items()}
+            for k, p in pros.items()}
+
+
+def run(lt, torch, w, inputs, pros, gates=None, overlap=False):
+    log(f"  GPU block with prologue: {w.name} B{w.batch} H{w.heads} D{w.head_dim} Sv{w.video_len} "
+        f"La{w.audio_len} Lk{w.audio_kv_len} {next(iter(pros.values()))['pairing']}"
+        f"{' gated' if gates else ''}{' overlap' if overlap else ''}")
+    dev = {n: to_device(a) for n, a in inputs.items()}
+    dp = dev_prologues(torch, pros)
+    dg = {k: to_device(g) for k, g in gates.items()} if gates else None
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len, qk_prologue=True)
+    outs = ba(dev, w.audio_kv_len, prologues=dp, gates=dg, overlap=overlap)
+    torch.cuda.synchronize()
+    res = {k: to_numpy(v) for k, v in outs.items()}
+    ba.close()
+    return res
+
+
+def gates_for(w, seed):
+    rng = np.random.default_rng(seed)
+    rows = {"video_self": w.video_len, "audio_self": w.audio_len, "a2v": w.video_len, "v2a": w.audio_len}
+    return {k: synth.bf16_bits(rng.uniform(0, 1, (w.batch, rows[k], w.heads, w.head_dim)).astype(np.float32))
+            for k in KINDS}
+
+
+SMALL = [synth.WORKLOADS[1],                                              # D64: resident keys everywhere
+         synth.Workload(11, "ragged D128", 2, 3, 128, 1000, 77, 70),      # two-buffer D128, staged a2v
+         synth.Workload(12, "ragged D64", 1, 2, 64, 2100, 130, 129),      # two-buffer D64, ring D64 v2a
+         synth.Workload(17, "ring ragged", 2, 2, 128, 1100, 77, 70)]      # 256-query ring, split v2a
+
+
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_prologue_full_oracle(lt, torch, w, pairing):
+    inputs = synth.make_block_inputs(w)
+    pros = synth.make_prologues(w, pairing)
+    got = run(lt, torch, w, inputs, pros)
+    want = oracle.block_attention(inputs, w.audio_kv_len, prologues=pros)
+    for k in KINDS:
+        compare(got[k], want[k], f"{w.name} prologue {pairing} {k}")
+
+
+def test_prologue_shared_keys_gated_and_overlap(lt, torch):
+    """Video self and v2a name the same keys with the same k parameters (one
+    key pass serves both; likewise audio self and a2v), with output gates; the
+    concurrent call's outputs equal the sequential call's bit for bit."""
+    w = SMALL[3]
+    inputs = synth.make_block_inputs(w)
+    pros = synth.make_prologues(w, "half", shared_k=True, seed=3)
+    gates = gates_for(w, 61)
+    seq = run(lt, torch, w, inputs, pros, gates=gates)
+    ovl = run(lt, torch, w, inputs, pros, gates=gates, overlap=True)
+    want = oracle.block_attention(inputs, w.audio_kv_len, prologues=pros, gates=gates)
+    for k in KINDS:
+        compare(seq[k], want[k], f"shared keys, gated {k}")
+        assert np.array_equal(seq[k], ovl[k]), k
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_prologue_unstaged_resident_keys(lt, torch, gated):
+    """200 valid audio keys: a2v on 8 register-Q waves, audio self on 4."""
+    w = synth.Workload(53, "resident 200 audio keys", 1, 32, 128, 2048, 256, 200)
+    inputs = synth.make_block_inputs(w)
+    pros = synth.make_prologues(w, "interleaved", seed=5)
+    gates = gates_for(w, 62) if gated else None
+    got = run(lt, torch, w, inputs, pros, gates=gates)
+    for k in ("a2v", "audio_self"):
+        q, kk, v, L = oracle.pairing(k, inputs, w.audio_kv_len)
+        q, kk = oracle.apply_prologue(q, kk, pros[k])
+        want = oracle.attention(q, kk, v, kv_len=L, gate=gates[k] if gated else None)
+        compare(got[k], want, f"{w.name} prologue{' gated' if gated else ''} {k}")
+
+
+def test_prologue_long_audio_two_buffer(lt, torch):
+    """600 audio keys: a2v and audio self-attention on the two-buffer kernel."""
+    w = synth.Workload(54, "600 audio keys", 1, 2, 128, 1500, 640, 600)
+    inputs = synth.make_block_inputs(w)
+    pros = synth.make_prologues(w, "half", seed=6)
+    got = run(lt, torch, w, inputs, pros)
+    want = oracle.block_attention(inputs, w.audio_kv_len, prologues=pros)
+    for k in KINDS:
+        compare(got[k], want[k], f"{w.name} prologue {k}")
+
+
+def test_prologue_full_size_every_item(lt, torch):
+    """The 768x1280x121 block (15360 video / 126 audio tokens, 32 heads of
+    128) with the prologue on every kind: one oracle row from every work item
+    of every kind."""
+    w = synth.WORKLOADS[3]
+    inputs = synth.make_block_inputs(w)
+    pros = synth.make_prologues(w, "half", seed=7)
+    got = run(lt, torch, w, inputs, pros)
+    rng = np.random.default_rng(7)
+    rows = {}
+    for k in KINDS:
+        Sq = w.video_len if k in ("video_self", "a2v") else w.audio_len
+        tile = 256 if k in ("video_self", "a2v") else 32
+        rows[k] = np.array([(0, h, int(rng.integers(t0, min(Sq, t0 + tile))))
+                            for h in range(w.heads) for t0 in range(0, Sq, tile)], np.int64)
+    want = oracle.block_attention_rows(inputs, w.audio_kv_len, rows, prologues=pros)
+    for k in KINDS:
+        r = rows[k]
+        compare(got[k][r[:, 0], r[:, 2], r[:, 1], :], want[k], f"cfg3 prologue every item {k}")
+
+
+def test_prologue_refused_without_workspace(lt, torch):
+    """A handle made without the key workspace, and the allocation-free call,
+    refuse a prologue before enqueuing anything."""
+    w = SMALL[0]
+    inputs = synth.make_block_inputs(w)
+    dev = {n: to_device(a) for n, a in inputs.items()}
+    dp = dev_prologues(torch, synth.make_prologues(w))
+    ba = lt.BlockAttention(w.heads, w.head_dim, w.batch, w.video_len, w.audio_len)
+    with pytest.raises(lt.LtxattnError) as e:
+        ba(dev, w.audio_kv_len, prologues=dp)
+    assert e.value.status == lt.LTXATTN_ERR_UNSUPPORTED
+    outs = {k: torch.empty_like(dev["video_q"] if k in ("video_self", "a2v") else dev["audio_q"]) for k in KINDS}
+    io = ba.make_io(dev, w.audio_kv_len, outs, prologues=dp)
+    cfg = lt.ltxattn_config(0, w.heads, w.head_dim, w.batch, w.video_len, w.audio_len, 1)
+    with pytest.raises(lt.LtxattnError) as e:
+        lt.ltxattn_block_attention_noalloc(cfg, io, torch.cuda.current_stream().cuda_stream)
+    assert e.value.status == lt.LTXATTN_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    ba.close()

@@ -70,6 +70,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 
 #include "ltxattn.h"
@@ -93,8 +94,22 @@ constexpr int NSPLIT_MAX = 16;   // key-range parts of a split work item
 constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int PROF_EVENTS = 14;         // per profiled block call, at most: start, end, 3 per kind
 
+// QK-norm + rotary prologue of the queries of one attention (w == null:
+// none): RMS norm of each (token, head) row over its D channels with the
+// per-channel weight w, then rotation of channel pairs -- (i, i + D/2), or
+// (2i, 2i + 1) when interleaved -- by the angle whose cosine and sine the
+// tables hold for pair i at the row's token.  Computed in fp32 and rounded
+// to bf16 where the queries are loaded.
+struct QkPrologue {
+    const float *w;           // [D]
+    const float *cos, *sin;   // [rows][D/2]
+    float eps;
+    int interleaved;
+};
+
 struct FaArgs {
     const __bf16 *q, *k, *v;
+    QkPrologue qp;    // of q
     int64_t q_sb, q_ss, q_sh;
     int64_t k_sb, k_ss, k_sh;
     int64_t v_sb, v_ss, v_sh;
@@ -178,6 +193,210 @@ __device__ __forceinline__ float xhalf_max(float x) {
 __device__ __forceinline__ float xhalf_sum(float x) {
     auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *(const f32x4 *)p; }
+
+// The prologue on one query row held as MFMA B-operand fragments: qf[k] is
+// channels 8(2k + hw) .. +7 of this lane's row (the lane of the other
+// half-wave holds the other chunks), so the row's sum of squares takes one
+// exchange between the half-waves, and both channels of every pair are in
+// the same lane -- chunk k pairs with chunk k + KS/2 (channel + D/2), or a
+// pair is two neighbours within a chunk.  In two steps, so that a kernel
+// can issue the loads of the weights and of the row's table entries early
+// and apply them once its queries have arrived: q_prologue_load fills the
+// lane's D/4 float4 of weights and table entries for table row `row`,
+// q_prologue_apply normalises, rotates and rounds qf in place.
+template <int D>
+__device__ __forceinline__ void q_prologue_load(const QkPrologue &p, int row, int hw, f32x4 *t) {
+    constexpr int KS = D / 16, P = D / 2;
+    const float *cs = p.cos + (int64_t)row * P, *sn = p.sin + (int64_t)row * P;
+    if (!p.interleaved) {
+#pragma unroll
+        for (int k = 0; k < KS / 2; ++k) {
+            const int d0 = 8 * (2 * k + hw);   // channels d0 .. d0+7 pair with d0+P ..
+            t[8 * k + 0] = ld4(p.w + d0);
+            t[8 * k + 1] = ld4(p.w + d0 + 4);
+            t[8 * k + 2] = ld4(p.w + d0 + P);
+            t[8 * k + 3] = ld4(p.w + d0 + P + 4);
+            t[8 * k + 4] = ld4(cs + d0);
+            t[8 * k + 5] = ld4(cs + d0 + 4);
+            t[8 * k + 6] = ld4(sn + d0);
+            t[8 * k + 7] = ld4(sn + d0 + 4);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const int c8 = 8 * (2 * k + hw);   // channels c8 .. c8+7 = pairs c8/2 .. c8/2+3
+            t[4 * k + 0] = ld4(p.w + c8);
+            t[4 * k + 1] = ld4(p.w + c8 + 4);
+            t[4 * k + 2] = ld4(cs + c8 / 2);
+            t[4 * k + 3] = ld4(sn + c8 / 2);
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void q_prologue_apply(const QkPrologue &p, bf16x8 *qf, const f32x4 *t) {
+    constexpr int KS = D / 16;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fmaf((float)qf[k][j], (float)qf[k][j], ss);
+    const float r = rsqrtf(fmaf(xhalf_sum(ss), 1.0f / D, p.eps));
+    if (!p.interleaved) {
+#pragma unroll
+        for (int k = 0; k < KS / 2; ++k)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int h = j / 4, e = j % 4;
+                const float ya = (float)qf[k][j] * r * t[8 * k + h][e];
+                const float yc = (float)qf[k + KS / 2][j] * r * t[8 * k + 2 + h][e];
+                const float cj = t[8 * k + 4 + h][e], sj = t[8 * k + 6 + h][e];
+                qf[k][j] = (__bf16)(ya * cj - yc * sj);
+                qf[k + KS / 2][j] = (__bf16)(ya * sj + yc * cj);
+            }
+    } else {
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float ya = (float)qf[k][2 * j] * r * t[4 * k + j / 2][(2 * j) % 4];
+                const float yc = (float)qf[k][2 * j + 1] * r * t[4 * k + j / 2][(2 * j + 1) % 4];
+                const float cj = t[4 * k + 2][j], sj = t[4 * k + 3][j];
+                qf[k][2 * j] = (__bf16)(ya * cj - yc * sj);
+                qf[k][2 * j + 1] = (__bf16)(ya * sj + yc * cj);
+            }
+    }
+}
+
+// The same in one step, a quarter of the weights and table entries at a
+// time (scheduling barriers keep the compiler from loading them all at
+// once), for kernels whose registers are mostly taken.
+template <int D>
+__device__ __forceinline__ void q_prologue(const QkPrologue &p, bf16x8 *qf, int row, int hw) {
+    constexpr int KS = D / 16, P = D / 2;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fmaf((float)qf[k][j], (float)qf[k][j], ss);
+    const float r = rsqrtf(fmaf(xhalf_sum(ss), 1.0f / D, p.eps));
+    const float *cs = p.cos + (int64_t)row * P, *sn = p.sin + (int64_t)row * P;
+    if (!p.interleaved) {
+#pragma unroll
+        for (int k = 0; k < KS / 2; ++k) {
+            const int d0 = 8 * (2 * k + hw);
+            const f32x4 wa[2] = {ld4(p.w + d0), ld4(p.w + d0 + 4)}, wc[2] = {ld4(p.w + d0 + P), ld4(p.w + d0 + P + 4)};
+            const f32x4 c[2] = {ld4(cs + d0), ld4(cs + d0 + 4)}, sv[2] = {ld4(sn + d0), ld4(sn + d0 + 4)};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float ya = (float)qf[k][j] * r * wa[j / 4][j % 4];
+                const float yc = (float)qf[k + KS / 2][j] * r * wc[j / 4][j % 4];
+                const float cj = c[j / 4][j % 4], sj = sv[j / 4][j % 4];
+                qf[k][j] = (__bf16)(ya * cj - yc * sj);
+                qf[k + KS / 2][j] = (__bf16)(ya * sj + yc * cj);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const int c8 = 8 * (2 * k + hw);
+            const f32x4 w[2] = {ld4(p.w + c8), ld4(p.w + c8 + 4)};
+            const f32x4 c = ld4(cs + c8 / 2), sv = ld4(sn + c8 / 2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float ya = (float)qf[k][2 * j] * r * w[j / 2][(2 * j) % 4];
+                const float yc = (float)qf[k][2 * j + 1] * r * w[j / 2][(2 * j + 1) % 4];
+                qf[k][2 * j] = (__bf16)(ya * c[j] - yc * sv[j]);
+                qf[k][2 * j + 1] = (__bf16)(ya * sv[j] + yc * c[j]);
+            }
+            if (k % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// The prologue as a pass of its own, for keys (which reach LDS by DMA, with
+// no register stage to fuse it into): y = prologue(x), [B][S][H][D] bf16
+// contiguous.  A lane holds 8 consecutive channels (16-byte loads and
+// stores), D/8 lanes a (b, s, h) row; rotate-half partners sit D/16 lanes
+// apart and trade values by one exchange.  Each wave takes PASS_UNROLL row
+// groups at a time, issuing all their loads first.
+struct PrologueRowsArgs {
+    const __bf16 *x;
+    int64_t x_sb, x_ss, x_sh;
+    __bf16 *y;
+    QkPrologue p;
+    int S, H;
+    int64_t rows;   // B * S * H
+};
+
+constexpr int PASS_UNROLL = 4;
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void qk_prologue_kernel(const PrologueRowsArgs a) {
+    constexpr int LPR = D / 8, RPW = 64 / LPR, P = D / 2;   // lanes per row, rows per wave
+    const int lane = threadIdx.x & 63, c = lane % LPR, d0 = 8 * c;
+    const bool lower = d0 < P;                              // rotate-half: holds the first channel of its pairs
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const f32x4 w0 = ld4(a.p.w + d0), w1 = ld4(a.p.w + d0 + 4);
+    for (int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); wv * RPW * PASS_UNROLL < a.rows;
+         wv += nwaves) {
+        bf16x8 xv[PASS_UNROLL];
+        f32x4 cs[PASS_UNROLL][2], sn[PASS_UNROLL][2];
+        int64_t rr[PASS_UNROLL];
+#pragma unroll
+        for (int u = 0; u < PASS_UNROLL; ++u) {
+            const int64_t row = (wv * PASS_UNROLL + u) * RPW + lane / LPR;
+            rr[u] = row < a.rows ? row : -1;
+            const int64_t r = row < a.rows ? row : a.rows - 1;
+            const int h = (int)(r % a.H), s = (int)((r / a.H) % a.S);
+            const int64_t b = r / ((int64_t)a.H * a.S);
+            xv[u] = *(const bf16x8 *)(a.x + b * a.x_sb + (int64_t)s * a.x_ss + (int64_t)h * a.x_sh + d0);
+            const float *ct = a.p.cos + (int64_t)s * P, *st = a.p.sin + (int64_t)s * P;
+            const int i0 = a.p.interleaved ? d0 / 2 : d0 % P;   // first pair index of the lane's channels
+            cs[u][0] = ld4(ct + i0);
+            sn[u][0] = ld4(st + i0);
+            if (!a.p.interleaved) {
+                cs[u][1] = ld4(ct + i0 + 4);
+                sn[u][1] = ld4(st + i0 + 4);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < PASS_UNROLL; ++u) {
+            float y[8], ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                y[j] = (float)xv[u][j];
+                ss = fmaf(y[j], y[j], ss);
+            }
+#pragma unroll
+            for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
+            const float r = rsqrtf(fmaf(ss, 1.0f / D, a.p.eps));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] = y[j] * r * (j < 4 ? w0[j] : w1[j - 4]);
+            bf16x8 out;
+            if (a.p.interleaved) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float cj = cs[u][0][j], sj = sn[u][0][j];
+                    out[2 * j] = (__bf16)(y[2 * j] * cj - y[2 * j + 1] * sj);
+                    out[2 * j + 1] = (__bf16)(y[2 * j] * sj + y[2 * j + 1] * cj);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float other = __shfl_xor(y[j], LPR / 2, 64);   // the partner channel, D/2 away
+                    const float cj = cs[u][j / 4][j % 4], sj = sn[u][j / 4][j % 4];
+                    out[j] = (__bf16)(lower ? y[j] * cj - other * sj : other * sj + y[j] * cj);
+                }
+            }
+            if (rr[u] >= 0) *(bf16x8 *)(a.y + rr[u] * D + d0) = out;
+        }
+    }
 }
 
 // Wait for all of this wave's outstanding memory loads (including DMA into
@@ -452,6 +671,7 @@ void fa_fwd_kernel(const FaArgs a) {
             qr, (int)((int64_t)qrow * a.q_ss * 2) + (2 * k + hw) * 16, 0, 0));
         qf[k] = __builtin_bit_cast(bf16x8, w);
     }
+    if (a.qp.w) q_prologue<D>(a.qp, qf, min(qrow, a.Sq - 1), hw);
 
     RowState<D> st;
 #pragma unroll
@@ -556,11 +776,11 @@ __device__ __forceinline__ void ring_barrier() {
 // refill waits for it at its first V read of the step; with LW = NW / 2 the
 // loads come from the waves that run behind their SIMD partners and reach
 // that read latest.
-template <int D, int NW, int NK, int LW>
+template <int D, int NW, int NK, int LW, class Pre>
 __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D, NW> &lo,
                                           const LaneOffsets<D, LW> &ldo, const bf16x8 *qf,
                                           RowState<D> &st, int kv_begin, int ntiles, int koff, int key0,
-                                          __amdgpu_buffer_rsrc_t none,
+                                          __amdgpu_buffer_rsrc_t none, Pre &&pre,
                                           LDS_AS char *__restrict__ K0, LDS_AS char *__restrict__ K1,
                                           LDS_AS char *__restrict__ K2, LDS_AS char *__restrict__ K3,
                                           LDS_AS char *__restrict__ V0, LDS_AS char *__restrict__ V1,
@@ -719,6 +939,7 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
     load(0, 0 < ntiles, K0, V0);
     load(1, 1 < ntiles, K1, V1);
     load(2, 2 < ntiles, K2, V2);
+    pre();                          // work on Q before the first wait for tiles
     ring_barrier<2 * PER_TILE>();   // Q and tile 0
     f32x16 sA[NKB], sB[NKB];
     scores<D, NW, NK>(lo, qf, K0 + koff, sA);
@@ -740,7 +961,7 @@ __device__ __forceinline__ void ring_loop(const TileCtx &x, const LaneOffsets<D,
     ring_barrier<0>();
 }
 
-template <int D, int NW, int KG>
+template <int D, int NW, int KG, bool QP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2)))
 void fa_ring_kernel(const FaArgs a) {
     constexpr int QW = NW / KG;                 // waves per key group = 32-query blocks per item
@@ -829,6 +1050,8 @@ void fa_ring_kernel(const FaArgs a) {
     for (int k = 0; k < KS; ++k)
         qf[k] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
             qr, (int)((int64_t)qrow * a.q_ss * 2) + (2 * k + hw) * 16, 0, 0));
+    f32x4 qtab[QP ? D / 4 : 1];
+    if constexpr (QP) q_prologue_load<D>(a.qp, min(qrow, a.Sq - 1), hw, qtab);
     const int ntiles = (x.kv_end - kv_begin + BN - 1) / BN;
     asm volatile("" ::: "memory");   // Q's loads stay ahead of the tiles'
 
@@ -837,8 +1060,10 @@ void fa_ring_kernel(const FaArgs a) {
     for (int i = 0; i < NDB; ++i) st.o[i] = f32x16{};
     st.m = -1e30f;
     st.l = 0.f;
+    // The query prologue runs while the ring's first tiles are on their way.
+    auto pre = [&]() { if constexpr (QP) q_prologue_apply<D>(a.qp, qf, qtab); };
     ring_loop<D, NW, NK, LW>(x, lo, ldo, qf, st, kv_begin, ntiles, group * NK * 2 * D, kv_begin + group * NK, none,
-                         lds, lds + TILE, lds + 2 * TILE, lds + 3 * TILE,
+                         pre, lds, lds + TILE, lds + 2 * TILE, lds + 3 * TILE,
                          lds + 4 * TILE, lds + 5 * TILE, lds + 6 * TILE, lds + 7 * TILE);
 
     float l_tot = xhalf_sum(st.l);
@@ -919,7 +1144,7 @@ void fa_ring_kernel(const FaArgs a) {
 // No workgroup barrier is needed except when the head changes.
 constexpr int KVRES_SLOT = 32 * 128 * 2;   // one wave's 32 rows of Q or O at D = 128 (8 KB)
 
-template <int D, int NW, bool STAGED, bool GATED>
+template <int D, int NW, bool STAGED, bool GATED, bool QP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2)))
 void fa_kvres_kernel(const FaArgs a) {
     constexpr int BM = 32 * NW, KS = D / 16, NDB = D / 32, NKB = BN / 32, PS = BN / 16;
@@ -1037,6 +1262,7 @@ void fa_kvres_kernel(const FaArgs a) {
             regs_q(item + 1, qn);
         }
 
+        if constexpr (QP) q_prologue<D>(a.qp, qf, min(q_row0(item) + l32, a.Sq - 1), hw);
         RowState<D> st;
 #pragma unroll
         for (int i = 0; i < NDB; ++i) st.o[i] = f32x16{};
@@ -1233,6 +1459,27 @@ void fill_args(FaArgs &a, const ltxattn_attn_io &io, int B, int H, int D, int Sq
     a.g_sb = io.gate.stride_b; a.g_ss = io.gate.stride_s; a.g_sh = io.gate.stride_h;
     a.B = B; a.H = H; a.Sq = Sq; a.kv_len = kv_len;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    const ltxattn_qk_prologue &pro = io.prologue;
+    if (pro.q_weight)
+        a.qp = QkPrologue{pro.q_weight, pro.q_cos, pro.q_sin, pro.eps, pro.pairing == LTXATTN_ROPE_INTERLEAVED};
+}
+
+// The resident-key kernel's instantiation.  Gated outputs and the query
+// prologue take instantiations of their own, so that the plain one is
+// compiled without any of their code (a uniform branch in its item loop
+// costs registers the staged variant does not have).
+template <int D, int NW, bool ST>
+const void *kvres_variant(bool gated, bool qp) {
+    if (gated)
+        return qp ? (const void *)&fa_kvres_kernel<D, NW, ST, true, true> : (const void *)&fa_kvres_kernel<D, NW, ST, true, false>;
+    return qp ? (const void *)&fa_kvres_kernel<D, NW, ST, false, true> : (const void *)&fa_kvres_kernel<D, NW, ST, false, false>;
+}
+
+const void *kvres_kernel(int D, int nw, bool staged, bool gated, bool qp) {
+    if (D == 128 && staged) return kvres_variant<128, 8, true>(gated, qp);
+    if (D == 128 && nw == 8) return kvres_variant<128, 8, false>(gated, qp);
+    if (D == 128) return kvres_variant<128, 4, false>(gated, qp);
+    return kvres_variant<64, 4, false>(gated, qp);
 }
 
 // a2v and audio self-attention: all keys resident in LDS, query tiles streamed.
@@ -1259,17 +1506,7 @@ Plan plan_resident_kv(int num_cus, int H, int D, const ltxattn_attn_io &io, int 
     const int per_group = std::min(a.ipg, (nw == 8 ? 1 : per_cu) * num_cus / a.groups);
     a.total = a.groups * per_group;
     p.threads = 64 * nw;
-    // Gated outputs take instantiations of their own, so that the ungated
-    // ones are compiled without any gate code.
-    const bool g = a.g != nullptr;
-    if (D == 128 && staged)
-        p.kernel = g ? (const void *)&fa_kvres_kernel<128, 8, true, true> : (const void *)&fa_kvres_kernel<128, 8, true, false>;
-    else if (D == 128 && nw == 8)
-        p.kernel = g ? (const void *)&fa_kvres_kernel<128, 8, false, true> : (const void *)&fa_kvres_kernel<128, 8, false, false>;
-    else if (D == 128)
-        p.kernel = g ? (const void *)&fa_kvres_kernel<128, 4, false, true> : (const void *)&fa_kvres_kernel<128, 4, false, false>;
-    else
-        p.kernel = g ? (const void *)&fa_kvres_kernel<64, 4, false, true> : (const void *)&fa_kvres_kernel<64, 4, false, false>;
+    p.kernel = kvres_kernel(D, nw, staged, a.g != nullptr, a.qp.w != nullptr);
     return p;
 }
 
@@ -1298,7 +1535,9 @@ Plan plan_stream(int num_cus, int H, int D, const ltxattn_attn_io &io, int B, in
     a.total = items * ns;
     p.threads = 64 * RING_NW;
     p.lds = (size_t)RING_STAGES * 2 * BN * D * 2;
-    p.kernel = D == 128 ? (const void *)&fa_ring_kernel<128, RING_NW, 2> : (const void *)&fa_ring_kernel<64, RING_NW, 2>;
+    const bool qp = a.qp.w != nullptr;
+    p.kernel = D == 128 ? (qp ? (const void *)&fa_ring_kernel<128, RING_NW, 2, true> : (const void *)&fa_ring_kernel<128, RING_NW, 2>)
+                        : (qp ? (const void *)&fa_ring_kernel<64, RING_NW, 2, true> : (const void *)&fa_ring_kernel<64, RING_NW, 2>);
     if (ns > 1) {
         p.region = REGION_V2A;
         p.ws_rows = (int64_t)items * ns * BM;
@@ -1362,7 +1601,7 @@ Plan plan_kind(int num_cus, int H, int D, const ltxattn_attn_io &io, int B, int 
         p.n_split_items = n_split_items;
     }
     if (D == 128 && NW == 8) {
-        p.kernel = (const void *)&fa_ring_kernel<128, RING_NW, 1>;
+        p.kernel = a.qp.w ? (const void *)&fa_ring_kernel<128, RING_NW, 1, true> : (const void *)&fa_ring_kernel<128, RING_NW, 1>;
         p.threads = 64 * RING_NW;
         p.lds = (size_t)RING_STAGES * 2 * BN * 128 * 2;
     } else {
@@ -1391,6 +1630,80 @@ void plan_block(const ltxattn_config &caps, const ltxattn_block_io *io, const bo
     }
 }
 
+// The prologue of one kind: every pointer given and 16-byte aligned, eps a
+// positive number, a known pairing.
+int check_prologue(const ltxattn_qk_prologue &p) {
+    const void *ptrs[6] = {p.q_weight, p.k_weight, p.q_cos, p.q_sin, p.k_cos, p.k_sin};
+    for (const void *q : ptrs)
+        if (!q || (uintptr_t)q % 16) return LTXATTN_ERR_INVALID_ARG;
+    if (!(p.eps > 0.f) || !std::isfinite(p.eps)) return LTXATTN_ERR_INVALID_ARG;
+    if (p.pairing != LTXATTN_ROPE_HALF && p.pairing != LTXATTN_ROPE_INTERLEAVED) return LTXATTN_ERR_INVALID_ARG;
+    return LTXATTN_OK;
+}
+
+bool has_prologue(const ltxattn_block_io *io, int k) { return io->attn[k].prologue.q_weight != nullptr; }
+
+// One prologue pass over a kind's keys, into a slot of the key workspace.
+struct KeyPass {
+    PrologueRowsArgs a;
+    int blocks;
+};
+
+// The key workspace: slots 0 and 1 hold video-sized keys, 2 and 3
+// audio-sized ones, each [batch][rows][heads][head_dim] bf16.
+struct KeyWorkspace {
+    __bf16 *base;
+    int64_t video_elems, audio_elems;   // per slot
+    __bf16 *slot(int i) const { return base + (i < 2 ? i * video_elems : 2 * video_elems + (i - 2) * audio_elems); }
+};
+
+// The key passes of a call, and each prologue kind's plan pointed at its
+// prepared keys.  Kinds whose keys are the same tensor under the same k
+// parameters share one pass.  Video keys (video self, v2a) take slots 0-1,
+// audio keys (audio self, a2v) slots 2-3.
+int plan_key_passes(const ltxattn_block_io *io, const bool on[4], int H, int D, const KeyWorkspace &kw,
+                    Plan plans[4], KeyPass passes[4]) {
+    int n = 0, slot_of[4] = {-1, -1, -1, -1}, next[2] = {0, 2};
+    const int B = io->batch;
+    for (int k = 0; k < 4; ++k) {
+        if (!on[k] || !has_prologue(io, k)) continue;
+        const bool video = k == LTXATTN_VIDEO_SELF || k == LTXATTN_V2A;
+        const int S = video ? io->video_len : io->audio_len;
+        const ltxattn_tensor &kt = io->attn[k].k;
+        const ltxattn_qk_prologue &p = io->attn[k].prologue;
+        int slot = -1;
+        for (int j = 0; j < k && slot < 0; ++j) {
+            if (slot_of[j] < 0 || (j == LTXATTN_VIDEO_SELF || j == LTXATTN_V2A) != video) continue;
+            const ltxattn_tensor &jt = io->attn[j].k;
+            const ltxattn_qk_prologue &q = io->attn[j].prologue;
+            if (jt.data == kt.data && jt.stride_b == kt.stride_b && jt.stride_s == kt.stride_s &&
+                jt.stride_h == kt.stride_h && q.k_weight == p.k_weight && q.k_cos == p.k_cos &&
+                q.k_sin == p.k_sin && q.eps == p.eps && q.pairing == p.pairing)
+                slot = slot_of[j];
+        }
+        if (slot < 0) {
+            slot = next[video ? 0 : 1]++;
+            KeyPass &kp = passes[n++];
+            kp.a.x = (const __bf16 *)kt.data;
+            kp.a.x_sb = kt.stride_b; kp.a.x_ss = kt.stride_s; kp.a.x_sh = kt.stride_h;
+            kp.a.y = kw.slot(slot);
+            kp.a.p = QkPrologue{p.k_weight, p.k_cos, p.k_sin, p.eps, p.pairing == LTXATTN_ROPE_INTERLEAVED};
+            kp.a.S = S;
+            kp.a.H = H;
+            kp.a.rows = (int64_t)B * S * H;
+            const int64_t waves = (kp.a.rows * (D / 8) + 64 * PASS_UNROLL - 1) / (64 * PASS_UNROLL);
+            kp.blocks = (int)std::min<int64_t>((waves + 3) / 4, 16384);
+        }
+        slot_of[k] = slot;
+        FaArgs &a = plans[k].a;
+        a.k = kw.slot(slot);
+        a.k_ss = (int64_t)H * D;
+        a.k_sh = D;
+        a.k_sb = (int64_t)S * H * D;
+    }
+    return n;
+}
+
 // Argument checks shared by ltxattn_check_block and the block calls, then
 // the workspace each kind's split parts need against the rows a workspace
 // for num_cus compute units has per region.  on[k] is set for the kinds
@@ -1416,6 +1729,10 @@ int validate_block(const ltxattn_config &caps, const ltxattn_block_io *io, int n
         if ((rc = check_tensor(x.v, B, kv_rows[k], H, D, false, &in_ext[k][2]))) return rc;
         if ((rc = check_tensor(x.o, B, q_rows[k], H, D, true, &out_ext[k]))) return rc;
         if (x.gate.data && (rc = check_tensor(x.gate, B, q_rows[k], H, D, false, &in_ext[k][3]))) return rc;
+        if (has_prologue(io, k)) {
+            if ((rc = check_prologue(x.prologue))) return rc;
+            if (!caps.qk_prologue) return LTXATTN_ERR_UNSUPPORTED;
+        }
     }
     for (int k = 0; k < 4; ++k) {
         if (!on[k]) continue;
@@ -1445,11 +1762,13 @@ struct Workspace {
 
 struct ltxattn_handle {
     int device;
-    int heads, head_dim, max_batch, max_video_len, max_audio_len;
+    int heads, head_dim, max_batch, max_video_len, max_audio_len, qk_prologue;
     int num_cus;
     // Workspace of split items (hipMalloc at create), in two regions so that
     // v2a can run beside video self-attention.
     Workspace ws;
+    // Keys prepared by the QK-norm + rotary prologue (qk_prologue only).
+    KeyWorkspace kw;
     // ltxattn_block_attention_overlap: the stream the audio-side kinds run
     // on, and the events that fork it from and join it to the caller's.
     hipStream_t side;
@@ -1499,23 +1818,18 @@ int hip_fail(ltxattn_handle *h, hipError_t e) {
 // kernel keeps up to RESIDENT_KV_MAX keys of K and V (and, staged, the Q/O row
 // slots) in LDS, the ring kernels four K/V tile pairs.  For the current device.
 hipError_t set_kernel_lds_limits() {
-    const void *kvres[8] = {
-        (const void *)&fa_kvres_kernel<128, 8, true, false>, (const void *)&fa_kvres_kernel<128, 8, true, true>,
-        (const void *)&fa_kvres_kernel<128, 8, false, false>, (const void *)&fa_kvres_kernel<128, 8, false, true>,
-        (const void *)&fa_kvres_kernel<128, 4, false, false>, (const void *)&fa_kvres_kernel<128, 4, false, true>,
-        (const void *)&fa_kvres_kernel<64, 4, false, false>, (const void *)&fa_kvres_kernel<64, 4, false, true>};
     hipError_t e = hipSuccess;
-    for (int i = 0; i < 8 && e == hipSuccess; ++i)
-        e = hipFuncSetAttribute(kvres[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_ring_kernel<128, RING_NW, 2>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 128 * 2);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_ring_kernel<64, RING_NW, 2>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 64 * 2);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)&fa_ring_kernel<128, RING_NW, 1>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, RING_STAGES * 2 * BN * 128 * 2);
+    for (int v = 0; v < 16 && e == hipSuccess; ++v) {   // (D, waves, staged) x gated x prologue
+        const int shape = v >> 2;
+        e = hipFuncSetAttribute(kvres_kernel(shape == 3 ? 64 : 128, shape == 2 ? 4 : 8, shape == 0, v & 1, v & 2),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+    }
+    const void *ring[6] = {(const void *)&fa_ring_kernel<128, RING_NW, 2>, (const void *)&fa_ring_kernel<128, RING_NW, 2, true>,
+                           (const void *)&fa_ring_kernel<128, RING_NW, 1>, (const void *)&fa_ring_kernel<128, RING_NW, 1, true>,
+                           (const void *)&fa_ring_kernel<64, RING_NW, 2>, (const void *)&fa_ring_kernel<64, RING_NW, 2, true>};
+    for (int i = 0; i < 6 && e == hipSuccess; ++i)
+        e = hipFuncSetAttribute(ring[i], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                RING_STAGES * 2 * BN * (i < 4 ? 128 : 64) * 2);
     return e;
 }
 
@@ -1567,12 +1881,14 @@ int launch_plan(ltxattn_handle *h, int D, const Plan &p, const Workspace &ws, hi
 int enqueue_block(ltxattn_handle *h, const ltxattn_block_io *io, hipStream_t st, bool overlap) {
     if (!h || !io) return LTXATTN_ERR_INVALID_ARG;
     const ltxattn_config caps = {h->device, h->heads, h->head_dim, h->max_batch, h->max_video_len,
-                                 h->max_audio_len};
+                                 h->max_audio_len, h->qk_prologue};
     bool on[4];
     const int vrc = validate_block(caps, io, h->num_cus, on);
     if (vrc) return vrc;
     Plan plans[4];
     plan_block(caps, io, on, h->num_cus, plans);
+    KeyPass passes[4];
+    const int n_passes = plan_key_passes(io, on, h->heads, h->head_dim, h->kw, plans, passes);
 
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return hip_fail(h, g.err);
@@ -1597,6 +1913,16 @@ int enqueue_block(ltxattn_handle *h, const ltxattn_block_io *io, hipStream_t st,
     const bool all = h->prof_kinds == 0xFu;
     int8_t last_main = -1, last_side = -1;
     if (ev) pc->first = last_main = all ? record(st) : (int8_t)-1;
+    // The prologue passes over keys come first, on the caller's stream, so
+    // that both sides of the overlapped call find their keys prepared.
+    for (int i = 0; i < n_passes; ++i) {
+        void *args[] = {&passes[i].a};
+        if (e == hipSuccess)
+            e = hipLaunchKernel(h->head_dim == 128 ? (const void *)&qk_prologue_kernel<128>
+                                                   : (const void *)&qk_prologue_kernel<64>,
+                                dim3(passes[i].blocks), dim3(256), args, 0, st);
+    }
+    if (ev && n_passes > 0 && all) last_main = record(st);   // the first kind starts after them
     if (overlap) {
         if (e == hipSuccess) e = hipEventRecord(h->fork, st);
         if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
@@ -1648,6 +1974,7 @@ hipError_t release(ltxattn_handle *h) {
     if (h->join) keep(hipEventDestroy(h->join));
     if (h->fork) keep(hipEventDestroy(h->fork));
     if (h->side) keep(hipStreamDestroy(h->side));
+    if (h->kw.base) keep(hipFree(h->kw.base));
     if (h->ws.ml) keep(hipFree(h->ws.ml));
     if (h->ws.o) keep(hipFree(h->ws.o));
     free(h);
@@ -1733,6 +2060,7 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
     h->max_batch = cfg->max_batch;
     h->max_video_len = cfg->max_video_len;
     h->max_audio_len = cfg->max_audio_len;
+    h->qk_prologue = cfg->qk_prologue != 0;
 
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) { g_create_hip_error = (int)g.err; free(h); return LTXATTN_ERR_HIP; }
@@ -1748,6 +2076,12 @@ int ltxattn_create(const ltxattn_config *cfg, ltxattn_handle **out) {
     int status = LTXATTN_OK;
     e = hipMalloc((void **)&h->ws.o, (size_t)rows * h->head_dim * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void **)&h->ws.ml, (size_t)rows * 2 * sizeof(float));
+    if (e == hipSuccess && h->qk_prologue) {
+        const int64_t row = (int64_t)h->heads * h->head_dim;
+        h->kw.video_elems = (int64_t)h->max_batch * h->max_video_len * row;
+        h->kw.audio_elems = (int64_t)h->max_batch * h->max_audio_len * row;
+        e = hipMalloc((void **)&h->kw.base, (size_t)(2 * h->kw.video_elems + 2 * h->kw.audio_elems) * 2);
+    }
     if (e != hipSuccess) status = LTXATTN_ERR_OOM;
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
@@ -1803,10 +2137,12 @@ int ltxattn_block_attention_noalloc(const ltxattn_config *cfg, const ltxattn_blo
     NoallocDevice dev;
     int rc = noalloc_device(cfg->device, &dev);
     if (rc) return rc;
+    ltxattn_config caps = *cfg;
+    caps.qk_prologue = 0;   // no key workspace here
     bool on[4];
-    if ((rc = validate_block(*cfg, io, dev.num_cus, on))) return rc;
+    if ((rc = validate_block(caps, io, dev.num_cus, on))) return rc;
     Plan plans[4];
-    plan_block(*cfg, io, on, dev.num_cus, plans);
+    plan_block(caps, io, on, dev.num_cus, plans);
     // The scratch holds exactly the regions this call uses: TAIL then V2A.
     Workspace ws = {};
     for (int k = 0; k < 4; ++k)

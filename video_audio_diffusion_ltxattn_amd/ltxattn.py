@@ -36,6 +36,9 @@ LTXATTN_A2V = 2
 LTXATTN_V2A = 3
 LTXATTN_NUM_KINDS = 4
 LTXATTN_PROFILE_FLOATS = 9
+LTXATTN_ROPE_HALF = 0
+LTXATTN_ROPE_INTERLEAVED = 1
+PAIRINGS = {"half": LTXATTN_ROPE_HALF, "interleaved": LTXATTN_ROPE_INTERLEAVED}
 KIND_NAMES = ("video_self", "audio_self", "a2v", "v2a")
 KIND_INDEX = {n: i for i, n in enumerate(KIND_NAMES)}
 
@@ -43,7 +46,8 @@ KIND_INDEX = {n: i for i, n in enumerate(KIND_NAMES)}
 class ltxattn_config(ctypes.Structure):
     _fields_ = [("device", ctypes.c_int32), ("heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("max_batch", ctypes.c_int32),
-                ("max_video_len", ctypes.c_int32), ("max_audio_len", ctypes.c_int32)]
+                ("max_video_len", ctypes.c_int32), ("max_audio_len", ctypes.c_int32),
+                ("qk_prologue", ctypes.c_int32)]
 
 
 class ltxattn_tensor(ctypes.Structure):
@@ -51,10 +55,18 @@ class ltxattn_tensor(ctypes.Structure):
                 ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
 
 
+class ltxattn_qk_prologue(ctypes.Structure):
+    _fields_ = [("q_weight", ctypes.c_void_p), ("k_weight", ctypes.c_void_p),
+                ("q_cos", ctypes.c_void_p), ("q_sin", ctypes.c_void_p),
+                ("k_cos", ctypes.c_void_p), ("k_sin", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("pairing", ctypes.c_int32)]
+
+
 class ltxattn_attn_io(ctypes.Structure):
     _fields_ = [("q", ltxattn_tensor), ("k", ltxattn_tensor),
                 ("v", ltxattn_tensor), ("o", ltxattn_tensor),
-                ("gate", ltxattn_tensor)]   # gate.data = None: no output gate
+                ("gate", ltxattn_tensor),        # gate.data = None: no output gate
+                ("prologue", ltxattn_qk_prologue)]   # prologue.q_weight = None: none
 
 
 class ltxattn_block_io(ctypes.Structure):
@@ -203,6 +215,22 @@ def ltxattn_profile_end(h) -> None:
 
 
 # ------------------------------------------------------------ torch wrapper
+def _f32_ptr(t, what: str) -> int:
+    import torch
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise TypeError(f"{what}: expected a contiguous float32 tensor")
+    return t.data_ptr()
+
+
+def prologue_desc(p: dict) -> ltxattn_qk_prologue:
+    """The QK-norm + rotary prologue of one kind from a dict: q_weight, k_weight
+    (float32 [D]), q_cos, q_sin, k_cos, k_sin (float32 [rows, D/2]), eps and
+    pairing ("half" or "interleaved")."""
+    return ltxattn_qk_prologue(*(_f32_ptr(p[n], n) for n in ("q_weight", "k_weight", "q_cos", "q_sin",
+                                                              "k_cos", "k_sin")),
+                               float(p["eps"]), PAIRINGS[p["pairing"]])
+
+
 def tensor_desc(t) -> ltxattn_tensor:
     """Describe a torch bf16 tensor [B, S, H, D] (D contiguous) for the ABI."""
     import torch
@@ -223,8 +251,9 @@ class BlockAttention:
     """
 
     def __init__(self, heads: int, head_dim: int, max_batch: int, max_video_len: int,
-                 max_audio_len: int, device: int = 0):
-        self.cfg = ltxattn_config(device, heads, head_dim, max_batch, max_video_len, max_audio_len)
+                 max_audio_len: int, device: int = 0, qk_prologue: bool = False):
+        self.cfg = ltxattn_config(device, heads, head_dim, max_batch, max_video_len, max_audio_len,
+                                  int(qk_prologue))
         self.device = device
         self.handle = ltxattn_create(self.cfg)
 
@@ -240,10 +269,11 @@ class BlockAttention:
             pass
 
     def make_io(self, streams: dict, audio_kv_len: int, outs: dict, inputs: dict = None,
-                gates: dict = None) -> ltxattn_block_io:
+                gates: dict = None, prologues: dict = None) -> ltxattn_block_io:
         """streams: video_q/k/v, audio_q/k/v tensors; outs: {kind name: output tensor};
         inputs: optional {kind name: (q, k, v)} replacing that kind's stream tensors;
-        gates: optional {kind name: gate tensor of that output's shape}.
+        gates: optional {kind name: gate tensor of that output's shape};
+        prologues: optional {kind name: QK-norm + rotary parameters (prologue_desc)}.
         The struct holds raw device pointers: every tensor named here must stay
         alive until the work enqueued with it has completed."""
         vq, vk, vv = streams["video_q"], streams["video_k"], streams["video_v"]
@@ -257,18 +287,20 @@ class BlockAttention:
         for name, o in outs.items():
             q, k, v = pairs[name]
             g = (gates or {}).get(name)
+            pro = (prologues or {}).get(name)
             io.attn[KIND_INDEX[name]] = ltxattn_attn_io(tensor_desc(q), tensor_desc(k), tensor_desc(v),
                                                         tensor_desc(o),
-                                                        tensor_desc(g) if g is not None else ltxattn_tensor())
+                                                        tensor_desc(g) if g is not None else ltxattn_tensor(),
+                                                        prologue_desc(pro) if pro else ltxattn_qk_prologue())
         return io
 
     def __call__(self, streams: dict, audio_kv_len: int, kinds=KIND_NAMES, outs: dict = None,
-                 stream=None, overlap: bool = False, gates: dict = None) -> dict:
+                 stream=None, overlap: bool = False, gates: dict = None, prologues: dict = None) -> dict:
         import torch
         if outs is None:
             vq, aq = streams["video_q"], streams["audio_q"]
             outs = {k: torch.empty_like(vq if k in ("video_self", "a2v") else aq) for k in kinds}
-        io = self.make_io(streams, audio_kv_len, outs, gates=gates)
+        io = self.make_io(streams, audio_kv_len, outs, gates=gates, prologues=prologues)
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
         call = ltxattn_block_attention_overlap if overlap else ltxattn_block_attention
         call(self.handle, io, s.cuda_stream)

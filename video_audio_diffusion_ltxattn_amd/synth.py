@@ -151,3 +151,56 @@ def attention_bytes(w: Workload) -> dict:
         "a2v": row * (2 * Sv + 2 * La),
         "v2a": row * (2 * La + 2 * Sv),
     }
+
+
+# ------------------------------------------- QK-norm + rotary prologue inputs
+# The caller's side of the prologue: RMS-norm weights near 1 (as trained
+# norm weights are) and rotary tables per token position.  The pages bake
+# the tables of each latent grid into the DiT plan and give no frequencies;
+# these stand in for them: video tokens at (frame, row, column) of a latent
+# grid 40 columns wide and 24 rows high (the 768x1280 grid; other lengths
+# wrap the same way), the D/2 channel pairs split into three groups that
+# rotate with the frame, the row and the column; audio tokens along one
+# axis.  Angles theta = position * 10000^(-j/n) for pair j of a group of n.
+GRID_W, GRID_H = 40, 24
+
+
+def _angles_1d(pos: np.ndarray, n: int) -> np.ndarray:
+    return pos[:, None].astype(np.float64) * 10000.0 ** (-np.arange(n) / n)[None, :]
+
+
+def rope_tables(S: int, D: int, video: bool):
+    """cos, sin float32 [S, D/2] for S tokens of the video or the audio stream."""
+    P = D // 2
+    s = np.arange(S)
+    if video:
+        n_y = n_x = P // 3
+        n_t = P - n_y - n_x
+        th = np.concatenate([_angles_1d(s // (GRID_W * GRID_H), n_t),
+                             _angles_1d((s // GRID_W) % GRID_H, n_y),
+                             _angles_1d(s % GRID_W, n_x)], axis=1)
+    else:
+        th = _angles_1d(s, P)
+    return np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
+
+
+def make_prologues(w: Workload, pairing: str = "half", eps: float = 1e-6, shared_k: bool = False,
+                   seed: int = 0) -> dict:
+    """Per kind: q_weight, k_weight (float32 [D], 1 + 0.1 N(0,1), drawn per kind
+    and tensor, seed 1000*cfg + 700 + seed), the rotary tables of its query and
+    key streams, eps and the pairing.  shared_k: the kinds that read the same
+    keys (video self and v2a; audio self and a2v) share one k weight."""
+    rng = np.random.Generator(np.random.PCG64(1000 * w.cfg + 700 + seed))
+    D = w.head_dim
+    tabs = {"video": rope_tables(w.video_len, D, True), "audio": rope_tables(w.audio_len, D, False)}
+    q_of = {"video_self": "video", "audio_self": "audio", "a2v": "video", "v2a": "audio"}
+    kv_of = {"video_self": "video", "audio_self": "audio", "a2v": "audio", "v2a": "video"}
+    weight = lambda: (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    k_weights = {"video": weight(), "audio": weight()}
+    out = {}
+    for kind in ("video_self", "audio_self", "a2v", "v2a"):
+        qs, ks = q_of[kind], kv_of[kind]
+        out[kind] = {"q_weight": weight(), "k_weight": k_weights[ks] if shared_k else weight(),
+                     "q_cos": tabs[qs][0], "q_sin": tabs[qs][1], "k_cos": tabs[ks][0], "k_sin": tabs[ks][1],
+                     "eps": eps, "pairing": pairing}
+    return out
