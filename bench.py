@@ -254,8 +254,12 @@ def main():
     dpros = None
     if args.qknorm_rope:
         pros = synth.make_prologues(w, "half", shared_k=True)
-        dpros = {k: {n: (torch.from_numpy(v).to("cuda:0") if isinstance(v, np.ndarray) else v)
-                     for n, v in p.items()} for k, p in pros.items()}
+        seen = {}   # one device copy per distinct array: kinds sharing keys share one key pass
+        for p in pros.values():
+            for n, v in p.items():
+                if isinstance(v, np.ndarray) and id(v) not in seen:
+                    seen[id(v)] = torch.from_numpy(v).to("cuda:0")
+        dpros = {k: {n: seen.get(id(v), v) for n, v in p.items()} for k, p in pros.items()}
     io = ba.make_io(dev, w.audio_kv_len, outs, kind_inputs, gates, dpros)
     scratch = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device="cuda:0")
                if args.flush_mib else None)

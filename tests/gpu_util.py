@@ -28,6 +28,22 @@ def to_device(bits: np.ndarray, device="cuda:0"):
     return t.to(device)
 
 
+def prologues_to_device(pros: dict, device="cuda:0") -> dict:
+    """Device copies of the prologue arrays, one per distinct array: kinds that
+    share an array share its device pointer (the library runs one key pass for
+    kinds whose keys and k parameters are the same pointers)."""
+    import torch
+    seen = {}
+
+    def dev(v):
+        if not isinstance(v, np.ndarray):
+            return v
+        if id(v) not in seen:
+            seen[id(v)] = torch.from_numpy(v).to(device)
+        return seen[id(v)]
+    return {k: {n: dev(v) for n, v in p.items()} for k, p in pros.items()}
+
+
 def to_numpy(t) -> np.ndarray:
     import torch
     return t.detach().float().cpu().numpy().astype(np.float64)

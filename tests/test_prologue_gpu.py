@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import compare, log, to_device, to_numpy
+from tests.gpu_util import compare, log, prologues_to_device, to_device, to_numpy
 from video_audio_diffusion_ltxattn_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -38,8 +38,7 @@ def lt(torch):
 
 
 def dev_prologues(torch, pros):
-    return {k: {n: (torch.from_numpy(v).to("cuda:0") if isinstance(v, np.ndarray) else v) for n, v in p.items()}
-            for k, p in pros.items()}
+    return prologues_to_device(pros)
 
 
 def run(lt, torch, w, inputs, pros, gates=None, overlap=False):

@@ -271,7 +271,7 @@ __device__ __forceinline__ void q_prologue_apply(const QkPrologue &p, bf16x8 *qf
     }
 }
 
-// The same in one step, a quarter of the weights and table entries at a
+// The prologue in one step, a quarter of the weights and table entries at a
 // time (scheduling barriers keep the compiler from loading them all at
 // once), for kernels whose registers are mostly taken.
 template <int D>
@@ -320,81 +320,78 @@ __device__ __forceinline__ void q_prologue(const QkPrologue &p, bf16x8 *qf, int 
 
 // The prologue as a pass of its own, for keys (which reach LDS by DMA, with
 // no register stage to fuse it into): y = prologue(x), [B][S][H][D] bf16
-// contiguous.  A lane holds 8 consecutive channels (16-byte loads and
-// stores), D/8 lanes a (b, s, h) row; rotate-half partners sit D/16 lanes
-// apart and trade values by one exchange.  Each wave takes PASS_UNROLL row
-// groups at a time, issuing all their loads first.
+// contiguous.  One wave per token: a lane holds 8 consecutive channels
+// (16-byte loads and stores) of one head, D/8 lanes a head and 64/(D/8)
+// heads at a time, so the lane's table entries -- the same for every head of
+// the token -- are loaded once.  Rotate-half partners sit D/16 lanes apart
+// and trade values by one exchange.
 struct PrologueRowsArgs {
     const __bf16 *x;
     int64_t x_sb, x_ss, x_sh;
     __bf16 *y;
     QkPrologue p;
     int S, H;
-    int64_t rows;   // B * S * H
+    int64_t tokens;   // B * S
 };
 
-constexpr int PASS_UNROLL = 4;
+constexpr int PASS_UNROLL = 4;   // head groups whose loads are issued together
 
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void qk_prologue_kernel(const PrologueRowsArgs a) {
-    constexpr int LPR = D / 8, RPW = 64 / LPR, P = D / 2;   // lanes per row, rows per wave
-    const int lane = threadIdx.x & 63, c = lane % LPR, d0 = 8 * c;
+    constexpr int LPR = D / 8, HPW = 64 / LPR, P = D / 2;   // lanes per head, heads per wave
+    const int lane = threadIdx.x & 63, c = lane % LPR, hr = lane / LPR, d0 = 8 * c;
     const bool lower = d0 < P;                              // rotate-half: holds the first channel of its pairs
-    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int i0 = a.p.interleaved ? d0 / 2 : d0 % P;       // first pair index of the lane's channels
     const f32x4 w0 = ld4(a.p.w + d0), w1 = ld4(a.p.w + d0 + 4);
-    for (int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); wv * RPW * PASS_UNROLL < a.rows;
-         wv += nwaves) {
-        bf16x8 xv[PASS_UNROLL];
-        f32x4 cs[PASS_UNROLL][2], sn[PASS_UNROLL][2];
-        int64_t rr[PASS_UNROLL];
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); tok < a.tokens; tok += nwaves) {
+        const int s = (int)(tok % a.S);
+        const int64_t b = tok / a.S;
+        const float *ct = a.p.cos + (int64_t)s * P + i0, *st = a.p.sin + (int64_t)s * P + i0;
+        const f32x4 cs[2] = {ld4(ct), a.p.interleaved ? f32x4{} : ld4(ct + 4)};
+        const f32x4 sn[2] = {ld4(st), a.p.interleaved ? f32x4{} : ld4(st + 4)};
+        const __bf16 *xt = a.x + b * a.x_sb + (int64_t)s * a.x_ss + d0;
+        __bf16 *yt = a.y + tok * a.H * D + d0;
+        for (int h0 = 0; h0 < a.H; h0 += HPW * PASS_UNROLL) {
+            bf16x8 xv[PASS_UNROLL];
 #pragma unroll
-        for (int u = 0; u < PASS_UNROLL; ++u) {
-            const int64_t row = (wv * PASS_UNROLL + u) * RPW + lane / LPR;
-            rr[u] = row < a.rows ? row : -1;
-            const int64_t r = row < a.rows ? row : a.rows - 1;
-            const int h = (int)(r % a.H), s = (int)((r / a.H) % a.S);
-            const int64_t b = r / ((int64_t)a.H * a.S);
-            xv[u] = *(const bf16x8 *)(a.x + b * a.x_sb + (int64_t)s * a.x_ss + (int64_t)h * a.x_sh + d0);
-            const float *ct = a.p.cos + (int64_t)s * P, *st = a.p.sin + (int64_t)s * P;
-            const int i0 = a.p.interleaved ? d0 / 2 : d0 % P;   // first pair index of the lane's channels
-            cs[u][0] = ld4(ct + i0);
-            sn[u][0] = ld4(st + i0);
-            if (!a.p.interleaved) {
-                cs[u][1] = ld4(ct + i0 + 4);
-                sn[u][1] = ld4(st + i0 + 4);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < PASS_UNROLL; ++u) {
-            float y[8], ss = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                y[j] = (float)xv[u][j];
-                ss = fmaf(y[j], y[j], ss);
+            for (int u = 0; u < PASS_UNROLL; ++u) {
+                const int h = min(h0 + u * HPW + hr, a.H - 1);
+                xv[u] = *(const bf16x8 *)(xt + (int64_t)h * a.x_sh);
             }
 #pragma unroll
-            for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
-            const float r = rsqrtf(fmaf(ss, 1.0f / D, a.p.eps));
-#pragma unroll
-            for (int j = 0; j < 8; ++j) y[j] = y[j] * r * (j < 4 ? w0[j] : w1[j - 4]);
-            bf16x8 out;
-            if (a.p.interleaved) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float cj = cs[u][0][j], sj = sn[u][0][j];
-                    out[2 * j] = (__bf16)(y[2 * j] * cj - y[2 * j + 1] * sj);
-                    out[2 * j + 1] = (__bf16)(y[2 * j] * sj + y[2 * j + 1] * cj);
-                }
-            } else {
+            for (int u = 0; u < PASS_UNROLL; ++u) {
+                const int h = h0 + u * HPW + hr;
+                float y[8], ss = 0.f;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float other = __shfl_xor(y[j], LPR / 2, 64);   // the partner channel, D/2 away
-                    const float cj = cs[u][j / 4][j % 4], sj = sn[u][j / 4][j % 4];
-                    out[j] = (__bf16)(lower ? y[j] * cj - other * sj : other * sj + y[j] * cj);
+                    y[j] = (float)xv[u][j];
+                    ss = fmaf(y[j], y[j], ss);
                 }
+#pragma unroll
+                for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
+                const float r = rsqrtf(fmaf(ss, 1.0f / D, a.p.eps));
+#pragma unroll
+                for (int j = 0; j < 8; ++j) y[j] = y[j] * r * (j < 4 ? w0[j] : w1[j - 4]);
+                bf16x8 out;
+                if (a.p.interleaved) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float cj = cs[0][j], sj = sn[0][j];
+                        out[2 * j] = (__bf16)(y[2 * j] * cj - y[2 * j + 1] * sj);
+                        out[2 * j + 1] = (__bf16)(y[2 * j] * sj + y[2 * j + 1] * cj);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float other = __shfl_xor(y[j], LPR / 2, 64);   // the partner channel, D/2 away
+                        const float cj = cs[j / 4][j % 4], sj = sn[j / 4][j % 4];
+                        out[j] = (__bf16)(lower ? y[j] * cj - other * sj : other * sj + y[j] * cj);
+                    }
+                }
+                if (h < a.H) *(bf16x8 *)(yt + (int64_t)h * D) = out;
             }
-            if (rr[u] >= 0) *(bf16x8 *)(a.y + rr[u] * D + d0) = out;
         }
     }
 }
@@ -1690,9 +1687,8 @@ int plan_key_passes(const ltxattn_block_io *io, const bool on[4], int H, int D, 
             kp.a.p = QkPrologue{p.k_weight, p.k_cos, p.k_sin, p.eps, p.pairing == LTXATTN_ROPE_INTERLEAVED};
             kp.a.S = S;
             kp.a.H = H;
-            kp.a.rows = (int64_t)B * S * H;
-            const int64_t waves = (kp.a.rows * (D / 8) + 64 * PASS_UNROLL - 1) / (64 * PASS_UNROLL);
-            kp.blocks = (int)std::min<int64_t>((waves + 3) / 4, 16384);
+            kp.a.tokens = (int64_t)B * S;   // one wave per token
+            kp.blocks = (int)std::min<int64_t>((kp.a.tokens + 3) / 4, 16384);
         }
         slot_of[k] = slot;
         FaArgs &a = plans[k].a;
