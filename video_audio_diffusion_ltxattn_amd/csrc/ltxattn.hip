@@ -1127,18 +1127,181 @@ void fa_ring_kernel(const FaArgs a) {
 }
 
 // ------------------------------------------------ resident short key streams
+// One block of 32 queries (this wave's) against two key tiles held in LDS --
+// at most 128 keys: K tiles at K and K + TILE, V tiles at V and V + TILE,
+// rows past kv_end zero -- in one software-pipelined pass at D = 128: the
+// score MFMAs of tile 1 run beside the probabilities of tile 0, and the P V
+// MFMAs of tile 0 beside the probabilities of tile 1 (operand reads two
+// chunks ahead, scheduling barriers holding the interleave).  Tile 0 sets
+// the max; tile 1's probabilities are taken against it and checked with the
+// row-sum bound of the ring kernel, which takes tile 1's max and rescales
+// only when some lane's sum exceeds RESCALE_SUM.  st is overwritten.
+template <int D, int NW>
+__device__ __forceinline__ void kv2_block(const TileCtx &x, const LaneOffsets<D, NW> &lo, const bf16x8 *qf,
+                                          const LDS_AS char *__restrict__ K, const LDS_AS char *__restrict__ V,
+                                          RowState<D> &st) {
+    static_assert(D == 128, "two-tile pass at D = 128");
+    constexpr int KS = D / 16, NDB = D / 32, PS = BN / 16, TILE = BN * D * 2;
+    constexpr int LA = 2;
+    auto read_k = [&](const LDS_AS char *kt, int k, bf16x8 *op) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            op[kb] = __builtin_bit_cast(bf16x8, *(const LDS_AS u32x4 *)(kt + kb * 32 * 2 * D + lo.k_rd[k]));
+    };
+    // Chunk c of a tile's P V: k-step c / 2, d blocks 2 (c % 2) and 2 (c % 2) + 1.
+    auto read_v = [&](const LDS_AS char *vt, int c, bf16x8 *op) {
+        const int k = c >> 1, dbp = c & 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const LDS_AS char *vp = vt + lo.v_rd[2 * dbp + j] + k * 16 * 2 * D;
+            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)vp);
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vp + 8 * 2 * D));
+            op[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+    // k-step kk of a tile's probabilities, in P V B-operand order (as in the
+    // ring kernel), with its row sums.
+    auto prob_step = [&](const f32x16 *sv, int kk, float mc, bf16x8 *p, float &r0, float &r1) {
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int kb = kk >> 1, i = 2 * (kk & 1) + h;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                p[kk][4 * h + j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[kb][i * 4 + j], x.c, -mc));
+            r0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[kk][4 * h], p[kk][4 * h + 1]}, one, r0, false);
+            r1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[kk][4 * h + 2], p[kk][4 * h + 3]}, one, r1, false);
+        }
+    };
+    auto rowmax = [&](const f32x16 *sv) {
+        float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; e += 4) {
+                mx0 = fmaxf(fmaxf(mx0, sv[kb][e]), sv[kb][e + 1]);
+                mx1 = fmaxf(fmaxf(mx1, sv[kb][e + 2]), sv[kb][e + 3]);
+            }
+        return xhalf_max(fmaxf(mx0, mx1));
+    };
+    // Keys at or past kv_end get -inf.  Element 4i + j of block kb is key
+    // t0 + 32 kb + 8 i + 4 hw + j: a group of four is tested only if some
+    // lane's key in it may be past the end (uniform), against a per-lane
+    // limit that is redefined at every call, so that the compiler does not
+    // hoist the tests out of the item loop into spilled scalar masks.
+    auto mask = [&](int t0, f32x16 *sv) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int rem = x.kv_end - t0 - 32 * kb;   // valid keys of the block
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (8 * i + 7 >= rem) {
+                    int lim = rem - 8 * i - 4 * x.hw;
+                    asm volatile("" : "+v"(lim));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (j >= lim) sv[kb][4 * i + j] = -INFINITY;
+                }
+        }
+    };
+
+    // Tile 0: scores and max.
+    f32x16 s0[2], s1[2];
+    scores<D, NW>(lo, qf, K, s0);
+    mask(0, s0);
+    st.m = rowmax(s0);
+    const float mc = st.m * x.c;
+
+    // Scores of tile 1 beside the probabilities of tile 0 (half a k-step per chunk).
+    bf16x8 p0[PS], p1[PS];
+    float a0 = 0.f, a1 = 0.f;
+    {
+        bf16x8 kop[LA + 1][2];
+#pragma unroll
+        for (int c = 0; c < LA; ++c) read_k(K + TILE, c, kop[c]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < KS; ++c) {
+            if (c + LA < KS) read_k(K + TILE, c + LA, kop[(c + LA) % (LA + 1)]);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                s1[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[c % (LA + 1)][kb], qf[c],
+                                                                 c == 0 ? f32x16{} : s1[kb], 0, 0, 0);
+            if (c & 1) prob_step(s0, c >> 1, mc, p0, a0, a1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    mask(BN, s1);
+    st.l = a0 + a1;
+
+    // P V of tile 0 beside the probabilities of tile 1 against tile 0's max.
+    float b0 = 0.f, b1 = 0.f;
+    {
+        bf16x8 vop[LA + 1][2];
+#pragma unroll
+        for (int c = 0; c < LA; ++c) read_v(V, c, vop[c]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < 2 * PS; ++c) {
+            if (c + LA < 2 * PS) read_v(V, c + LA, vop[(c + LA) % (LA + 1)]);
+            const int k = c >> 1, dbp = c & 1;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                st.o[2 * dbp + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[c % (LA + 1)][j], p0[k],
+                                                                            c < 2 ? f32x16{} : st.o[2 * dbp + j], 0, 0, 0);
+            if (c & 1) prob_step(s1, c >> 1, mc, p1, b0, b1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    float rsum = b0 + b1;
+    if (__builtin_amdgcn_ballot_w64(!(rsum <= RESCALE_SUM))) {
+        const float m_new = fmaxf(st.m, rowmax(s1));
+        const float alpha = __builtin_amdgcn_exp2f((st.m - m_new) * x.c);
+        st.m = m_new;
+        st.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
+        const float mc1 = m_new * x.c;
+        b0 = b1 = 0.f;
+#pragma unroll
+        for (int k = 0; k < PS; ++k) prob_step(s1, k, mc1, p1, b0, b1);
+        rsum = b0 + b1;
+    }
+    st.l += rsum;
+
+    // P V of tile 1.
+    {
+        bf16x8 vop[LA + 1][2];
+#pragma unroll
+        for (int c = 0; c < LA; ++c) read_v(V + TILE, c, vop[c]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < 2 * PS; ++c) {
+            if (c + LA < 2 * PS) read_v(V + TILE, c + LA, vop[(c + LA) % (LA + 1)]);
+            const int k = c >> 1, dbp = c & 1;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                st.o[2 * dbp + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[c % (LA + 1)][j], p1[k], st.o[2 * dbp + j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 // a2v and audio self-attention have at most a few hundred (audio) keys: a
-// workgroup loads all K/V tiles of its head into LDS once and then streams
-// a contiguous range of query tiles (32 rows per wave) past them.  The kernel is bound by
-// reading Q and writing O, so both move as whole rows: each wave DMAs its 32
-// query rows into a wave-private LDS slot (1 KB = 4 rows per instruction),
-// takes its MFMA operands from there, and stages its output rows through
-// the same slot for 16-byte-per-lane row stores; the next tile's Q is
-// fetched after the stores, the other wave of the SIMD computing meanwhile
-// (STAGED, 8 waves, D = 128).  Otherwise (more keys than leave room for the
-// slots, or D = 64) the waves -- 8 at D = 128 for long query streams, two
-// per SIMD, else 4 -- take Q straight into registers, one tile ahead.
-// No workgroup barrier is needed except when the head changes.
+// workgroup loads all K/V tiles of its head into LDS once (K tiles, then V
+// tiles) and then streams a contiguous range of query tiles (32 rows per
+// wave) past them.  Q and O move as whole rows: with at most 128 keys
+// (STAGED, 8 waves, D = 128) each wave DMAs its 32 query rows into a
+// wave-private LDS slot (1 KB = 4 rows per instruction), takes its MFMA
+// operands from there, computes with kv2_block, and stages its output rows
+// through the same slot for 16-byte-per-lane row stores; the next tile's Q
+// is fetched after the stores, the other wave of the SIMD computing
+// meanwhile.  Otherwise (more keys, or D = 64) the waves -- 8 at D = 128 for
+// long query streams, two per SIMD, else 4 -- take Q straight into
+// registers, one tile ahead, and run the tiles one after another.  No
+// workgroup barrier is needed except when the head changes.
 constexpr int KVRES_SLOT = 32 * 128 * 2;   // one wave's 32 rows of Q or O at D = 128 (8 KB)
 
 template <int D, int NW, bool STAGED, bool GATED, bool QP = false>
@@ -1147,13 +1310,14 @@ void fa_kvres_kernel(const FaArgs a) {
     constexpr int BM = 32 * NW, KS = D / 16, NDB = D / 32, NKB = BN / 32, PS = BN / 16;
     constexpr int TILE = BN * D * 2;
     constexpr int ROWB = D * 2;             // bytes per Q/O row
-    extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];   // [kv tile][K, V] [wave][slot]
+    extern __shared__ __attribute__((aligned(1024))) char smem_dyn[];   // [K tiles][V tiles][wave slots]
     LDS_AS char *const lds = (LDS_AS char *)smem_dyn;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hw = lane >> 5, l32 = lane & 31;
-    const int nkt = (a.kv_len + BN - 1) / BN;
+    // STAGED holds two tiles (the rows past kv_len read as zeros), else every tile of the keys.
+    const int nkt = STAGED ? 2 : (a.kv_len + BN - 1) / BN;
     LDS_AS char *const slot = lds + nkt * 2 * TILE + wave * KVRES_SLOT;   // STAGED: this wave's Q/O rows
 
     // This workgroup's items: a contiguous share of its group's range (the
@@ -1200,22 +1364,41 @@ void fa_kvres_kernel(const FaArgs a) {
         return make_rsrc(a.q + b * a.q_sb + hh * a.q_sh, ((int64_t)(a.Sq - 1) * a.q_ss + D) * 2);
     };
     auto q_row0 = [&](int item) { return (item % a.n_qtiles) * BM + wave * 32; };
-    // 32 rows of this wave's query tile from a [B, Sq, H, D] tensor (Q, or
-    // the output gate) into a slot.
-    auto dma_rows = [&](int item, LDS_AS char *slot, const __bf16 *t, int64_t sb, int64_t ss, int64_t sh) {
+    // STAGED: the 32 rows of this wave's query tile in a [B, Sq, H, D] tensor
+    // (Q, the output gate or O) as a buffer resource that starts at the
+    // tile's first row; rows at or past Sq lie outside its range (loads read
+    // zeros, stores are dropped).  Lane offsets within it, the same for every
+    // item: chunk idx = n * 64 + lane of the slot is row idx / (D / 8),
+    // physical chunk idx % (D / 8), which holds the row's chunk swz_k of it.
+    constexpr int NRC = STAGED ? 32 * (D / 8) / 64 : 1;   // 16-byte chunks per lane
+    auto rows_rsrc = [&](int item, const __bf16 *t, int64_t sb, int64_t ss, int64_t sh) {
         const int bh = item / a.n_qtiles, b = bh / a.H, hh = bh % a.H;
-        const __amdgpu_buffer_rsrc_t tr = make_rsrc(t + b * sb + hh * sh, ((int64_t)(a.Sq - 1) * ss + D) * 2);
         const int r0 = q_row0(item);
+        const int64_t bytes = r0 < a.Sq ? ((int64_t)(a.Sq - 1 - r0) * ss + D) * 2 : 0;
+        return make_rsrc(t + b * sb + hh * sh + (int64_t)r0 * ss, bytes);
+    };
+    auto row_offsets = [&](int64_t ss, bool swizzled_src, int *off) {
 #pragma unroll
-        for (int n = 0; n < 32 * (D / 8) / 64; ++n) {
-            const int idx = n * 64 + lane;              // physical chunk in the slot
+        for (int n = 0; n < NRC; ++n) {
+            const int idx = n * 64 + lane;
             const int r = idx / (D / 8), p = idx % (D / 8);
-            const int c = swz_k<D>(r, p);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(tr, (LDS_AS void *)(slot + n * 1024), 16,
-                                                     (int)((int64_t)(r0 + r) * ss * 2) + c * 16, 0, 0, 0);
+            off[n] = r * (int)(ss * 2) + (swizzled_src ? swz_k<D>(r, p) : p) * 16;
         }
     };
-    auto dma_q = [&](int item, LDS_AS char *slot) { dma_rows(item, slot, a.q, a.q_sb, a.q_ss, a.q_sh); };
+    int q_off[NRC], g_off[GATED ? NRC : 1], o_off[NRC];
+    if constexpr (STAGED) {
+        row_offsets(a.q_ss, true, q_off);
+        if constexpr (GATED) row_offsets(a.g_ss, true, g_off);
+        row_offsets(a.o_ss, false, o_off);
+    }
+    auto dma_rows = [&](int item, LDS_AS char *slot, const __bf16 *t, int64_t sb, int64_t ss, int64_t sh,
+                        const int *off) {
+        const __amdgpu_buffer_rsrc_t tr = rows_rsrc(item, t, sb, ss, sh);
+#pragma unroll
+        for (int n = 0; n < NRC; ++n)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(tr, (LDS_AS void *)(slot + n * 1024), 16, off[n], 0, 0, 0);
+    };
+    auto dma_q = [&](int item, LDS_AS char *slot) { dma_rows(item, slot, a.q, a.q_sb, a.q_ss, a.q_sh, q_off); };
     auto regs_q = [&](int item, bf16x8 *qf) {
         const __amdgpu_buffer_rsrc_t qr = q_rsrc(item);
         const int qrow = q_row0(item) + l32;
@@ -1237,8 +1420,8 @@ void fa_kvres_kernel(const FaArgs a) {
             x.kr = make_rsrc(a.k + b * a.k_sb + hh * a.k_sh, ((int64_t)(a.kv_len - 1) * a.k_ss + D) * 2);
             x.vr = make_rsrc(a.v + b * a.v_sb + hh * a.v_sh, ((int64_t)(a.kv_len - 1) * a.v_ss + D) * 2);
             for (int t = 0; t < nkt; ++t) {
-                dma_tile<D, NW>(x.kr, lo.k_src, t * BN * x.k_stride, lds + (2 * t) * TILE, wave);
-                dma_tile<D, NW>(x.vr, lo.v_src, t * BN * x.v_stride, lds + (2 * t + 1) * TILE, wave);
+                dma_tile<D, NW>(x.kr, lo.k_src, t * BN * x.k_stride, lds + t * TILE, wave);
+                dma_tile<D, NW>(x.vr, lo.v_src, t * BN * x.v_stride, lds + (nkt + t) * TILE, wave);
             }
             tile_barrier();   // also completes this wave's Q
             cur_bh = bh;
@@ -1253,7 +1436,7 @@ void fa_kvres_kernel(const FaArgs a) {
                     *(const LDS_AS u32x4 *)(slot + l32 * ROWB + swz_k<D>(l32, 2 * k + hw) * 16));
             if constexpr (GATED) {   // the gate rows of this tile take Q's place in the slot
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                dma_rows(item, slot, a.g, a.g_sb, a.g_ss, a.g_sh);
+                dma_rows(item, slot, a.g, a.g_sb, a.g_ss, a.g_sh, g_off);
             }
         } else if (item + 1 < i_end) {
             regs_q(item + 1, qn);
@@ -1265,16 +1448,20 @@ void fa_kvres_kernel(const FaArgs a) {
         for (int i = 0; i < NDB; ++i) st.o[i] = f32x16{};
         st.m = -1e30f;
         st.l = 0.f;
-        for (int t = 0; t < nkt; ++t) {
-            const LDS_AS char *kt = lds + (2 * t) * TILE;
-            const LDS_AS char *vt = lds + (2 * t + 1) * TILE;
-            f32x16 sc[NKB];
-            scores<D, NW>(lo, qf, kt, sc);
-            mask_tail(x, t * BN, sc);
-            update_max<D>(x, sc, st);
-            bf16x8 pf[PS];
-            probs<D>(x, sc, st, pf);
-            accumulate_pv<D, NW>(lo, vt, pf, st);
+        if constexpr (STAGED) {
+            kv2_block<D, NW>(x, lo, qf, lds, lds + 2 * TILE, st);
+        } else {
+            for (int t = 0; t < nkt; ++t) {
+                const LDS_AS char *kt = lds + t * TILE;
+                const LDS_AS char *vt = lds + (nkt + t) * TILE;
+                f32x16 sc[NKB];
+                scores<D, NW>(lo, qf, kt, sc);
+                mask_tail(x, t * BN, sc);
+                update_max<D>(x, sc, st);
+                bf16x8 pf[PS];
+                probs<D>(x, sc, st, pf);
+                accumulate_pv<D, NW>(lo, vt, pf, st);
+            }
         }
         const float inv = 1.0f / xhalf_sum(st.l);
         __bf16 *obase = a.o + b * a.o_sb + hh * a.o_sh;
@@ -1302,12 +1489,13 @@ void fa_kvres_kernel(const FaArgs a) {
                     }
                     *cell = ov;
                 }
+            const __amdgpu_buffer_rsrc_t orr = rows_rsrc(item, a.o, a.o_sb, a.o_ss, a.o_sh);
 #pragma unroll
-            for (int n = 0; n < 32 * (D / 8) / 64; ++n) {
+            for (int n = 0; n < NRC; ++n) {
                 const int idx = n * 64 + lane;
                 const int r = idx / (D / 8), c = idx % (D / 8);
                 const u32x4 w = *(const LDS_AS u32x4 *)(slot + r * ROWB + swz_k<D>(r, c) * 16);
-                if (qrow0 + r < a.Sq) *(u32x4 *)(obase + (int64_t)(qrow0 + r) * a.o_ss + c * 8) = w;
+                __builtin_amdgcn_raw_buffer_store_b128(w, orr, o_off[n], 0, 0);
             }
             if (item + 1 < i_end) {
                 // The slot's output rows have been read (the stores hold them); refill it.
@@ -1487,14 +1675,14 @@ Plan plan_resident_kv(int num_cus, int H, int D, const ltxattn_attn_io &io, int 
     const int nkt = ceil_div(kv_len, BN);
     const size_t kv_lds = (size_t)nkt * 2 * BN * D * 2;
     // D = 128: 8 waves, two per SIMD, with Q and O rows staged through one
-    // 8 KB slot per wave when the keys leave room for the slots, else with
-    // Q straight from HBM into registers (up to 256 keys: 128 KB of K/V) --
-    // or 4 such waves when 256-query items would leave most CUs idle (a
-    // short query stream such as audio self-attention).  D = 64: 4 unstaged
-    // waves.
-    const bool staged = D == 128 && kv_lds + 8 * KVRES_SLOT <= LDS_BYTES;
+    // 8 KB slot per wave and the two-tile pass when there are at most 128
+    // keys, else with Q straight from HBM into registers (up to 256 keys:
+    // 128 KB of K/V) -- or 4 such waves when 256-query items would leave
+    // most CUs idle (a short query stream such as audio self-attention).
+    // D = 64: 4 unstaged waves.
+    const bool staged = D == 128 && nkt <= 2;
     const int nw = staged || (D == 128 && (int64_t)B * H * ceil_div(Sq, 256) >= num_cus) ? 8 : 4;
-    p.lds = kv_lds + (staged ? (size_t)8 * KVRES_SLOT : 0);
+    p.lds = staged ? (size_t)2 * 2 * BN * D * 2 + (size_t)8 * KVRES_SLOT : kv_lds;
     a.n_qtiles = ceil_div(Sq, 32 * nw);
     const int items = B * H * a.n_qtiles;
     const int per_cu = (int)std::min<size_t>(2, LDS_BYTES / p.lds);   // LDS-resident workgroups per CU
