@@ -68,6 +68,10 @@ RAGGED = [
     synth.Workload(17, "ring ragged", 2, 2, 128, 1100, 77, 70),
     synth.Workload(18, "ring remainder 3", 1, 1, 128, 1215, 130, 129),
     synth.Workload(19, "ring remainder 1", 1, 3, 128, 1030, 16, 16),
+    # The two-tile pass of the resident-key kernel at its mask boundaries:
+    # one key into the second tile, and one key short of both tiles.
+    synth.Workload(20, "audio keys 65", 1, 2, 128, 300, 96, 65),
+    synth.Workload(22, "audio keys 127", 1, 2, 128, 300, 128, 127),
 ]
 
 
